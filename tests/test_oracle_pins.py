@@ -1,0 +1,324 @@
+"""Pins the CPU oracle to facts that do not come from the oracle itself:
+the printed i2_s code map (golden bytes), closed forms, brute force against a
+dense integer matmul, invariants of the mathematics, and exact rational
+arithmetic.  CPU only."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------- #
+# canonical i2_s pack / unpack
+# --------------------------------------------------------------------------- #
+def _golden_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "i2s_canonical_bytes.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, assign, expect = [s.strip() for s in line.split("|")]
+            rows.append((name, assign, expect))
+    return rows
+
+
+@pytest.mark.parametrize("name,assign,expect", _golden_rows())
+def test_pack_golden_bytes(name, assign, expect):
+    t = np.zeros((1, 128), np.int8)
+    for tok in assign.split():
+        k, v = tok.split("=")
+        if k == "fill":
+            t[:] = int(v)
+        else:
+            t[0, int(k)] = int(v)
+    P = oracle.pack_i2s(t)
+    for tok in expect.split():
+        j, hx = tok.split("=")
+        assert P[0, int(j)] == int(hx, 16), (name, j, hex(P[0, int(j)]))
+    assert np.array_equal(oracle.unpack_i2s(P, 128), t)
+
+
+def test_pack_exhaustive_quadruples():
+    # every one of the 81 (t0,t1,t2,t3) quadruples placed at weights j, 32+j, 64+j, 96+j
+    quads = np.array(np.meshgrid(*[[-1, 0, 1]] * 4, indexing="ij")).reshape(4, -1).T  # 81 x 4
+    T = np.zeros((81, 128), np.int8)
+    for r, qd in enumerate(quads):
+        j = r % 32
+        for g in range(4):
+            T[r, 32 * g + j] = qd[g]
+    P = oracle.pack_i2s(T)
+    for r, qd in enumerate(quads):
+        j = r % 32
+        want = sum((int(qd[g]) + 1) << (6 - 2 * g) for g in range(4))
+        assert P[r, j] == want
+    assert np.array_equal(oracle.unpack_i2s(P, 128), T)
+
+
+@pytest.mark.parametrize("N,K", [(2560, 2560), (13824, 2560), (20480, 3200), (2560, 6912), (16, 128)])
+def test_pack_roundtrip_config_shapes(N, K):
+    T = wl.ternary_uniform(wl.rng_for(7, N, K), N, K)
+    P = oracle.pack_i2s(T)
+    assert P.shape == (N, K // 4)
+    assert np.array_equal(oracle.unpack_i2s(P, K), T)
+
+
+def test_pack_rejects_non_ternary_and_code3():
+    T = np.zeros((1, 128), np.int8)
+    T[0, 5] = 2
+    with pytest.raises(ValueError):
+        oracle.pack_i2s(T)
+    P = np.full((1, 32), 0x55, np.uint8)
+    P[0, 3] = 0xFF  # code 3
+    with pytest.raises(ValueError):
+        oracle.unpack_i2s(P, 128)
+
+
+# --------------------------------------------------------------------------- #
+# activation quantisation
+# --------------------------------------------------------------------------- #
+def _acts(seed, M, K, t=False):
+    r = wl.rng_for(11, seed, M, K)
+    return wl.student_t_act(r, M, K) if t else wl.normal_act(r, M, K)
+
+
+@pytest.mark.parametrize("M,K,t", [(1, 2560, False), (8, 2560, False), (3, 3200, True), (5, 6912, False)])
+def test_quant_invariants(M, K, t):
+    xb = _acts(M + K, M, K, t)
+    x = wl.bf16_to_f32(xb)
+    q, s = oracle.quant_act_bf16(xb)
+    q2, s2 = oracle.quant_act_f32(x)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    for m in range(M):
+        am = np.abs(x[m]).max()
+        k0 = int(np.abs(x[m]).argmax())
+        assert abs(int(q[m, k0])) == 127 and np.sign(q[m, k0]) == np.sign(x[m, k0])
+        assert np.abs(q[m]).max() == 127
+        # dequant factor is amax/127 in fp32 (division correctly rounded: exact rational check)
+        assert Fraction(float(s[m])) == Fraction(float(np.float32(am) / np.float32(127)))
+        assert abs(Fraction(float(s[m])) - Fraction(float(am)) / 127) <= Fraction(float(s[m])) * Fraction(1, 2 ** 24)
+        # round-to-nearest reconstruction: |x - q*s| <= s/2 (up to fp32 rounding of the ratio)
+        err = np.abs(x[m].astype(np.float64) - q[m].astype(np.float64) * float(s[m]))
+        assert err.max() <= float(s[m]) * (0.5 + 1e-5)
+        # monotone in x
+        order = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(q[m][order].astype(np.int32)) >= 0)
+    # sign symmetry and power-of-two scale invariance
+    qn, sn = oracle.quant_act_f32(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for j in (-3, 5):
+        qj, sj = oracle.quant_act_f32(x * np.float32(2.0 ** j))
+        assert np.array_equal(qj, q)
+        assert np.array_equal(sj, (s * np.float32(2.0 ** j)).astype(np.float32))
+
+
+def test_quant_special_cases():
+    x = np.zeros((2, 256), np.float32)
+    x[1, 7] = -3.5
+    x[1, 9] = 1.75  # exactly half of amax -> 63.5 -> ties to even -> 64
+    x[1, 11] = 3.5 / 254.0 * 1.0  # tiny
+    q, s = oracle.quant_act_f32(x)
+    assert np.all(q[0] == 0)
+    assert s[0] == np.float32(np.float32(1e-5) / np.float32(127))
+    assert q[1, 7] == -127
+    inv = np.float32(127) / np.float32(3.5)
+    assert q[1, 9] == int(np.rint(np.float32(1.75) * inv))
+    assert int(np.rint(np.float32(1.75) * inv)) in (63, 64)
+
+
+def test_quant_matches_numpy_fp32():
+    # an independent evaluation with numpy's own fp32 division and rint
+    xb = _acts(3, 4, 2560)
+    x = wl.bf16_to_f32(xb)
+    q, s = oracle.quant_act_bf16(xb)
+    am = np.maximum(np.abs(x).max(axis=1), np.float32(1e-5)).astype(np.float32)
+    inv = (np.float32(127) / am).astype(np.float32)
+    qq = np.clip(np.rint((x * inv[:, None]).astype(np.float32)), -127, 127).astype(np.int8)
+    assert np.array_equal(q, qq)
+    assert np.array_equal(s, (am / np.float32(127)).astype(np.float32))
+
+
+# --------------------------------------------------------------------------- #
+# integer product
+# --------------------------------------------------------------------------- #
+def _brute(T, Q):
+    return (Q.astype(np.int64) @ T.astype(np.int64).T)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+@pytest.mark.parametrize("N,K", [(16, 128), (32, 256), (64, 384), (48, 640)])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_product_brute_force_tiny(M, N, K, seed):
+    c = wl.small_case(seed, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    r = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, s, N, K)
+    want = _brute(c.T, q)
+    assert np.array_equal(r["acc"].astype(np.int64), want)
+    assert np.array_equal(oracle.acc_dense(c.T, q).astype(np.int64), want)
+
+
+def test_product_brute_force_config_shape():
+    c = wl.config2(M=8)
+    T, S = oracle.ternarize_absmean(c.W)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    r = oracle.w2a8(oracle.pack_i2s(T), S, q, s, c.N, c.K)
+    assert np.array_equal(r["acc"].astype(np.int64), _brute(T, q))
+
+
+def test_product_invariants():
+    M, N, K = 3, 32, 512
+    c = wl.small_case(5, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    base = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, s, N, K)
+    # zero weights
+    z = oracle.w2a8(oracle.pack_i2s(np.zeros_like(c.T)), c.S, q, s, N, K)
+    assert np.all(z["acc"] == 0) and np.all(z["y"] == 0)
+    # all +1 row -> activation sum; one-hot row -> one activation
+    T2 = c.T.copy()
+    T2[3] = 1
+    T2[4] = 0
+    T2[4, 200] = 1
+    r2 = oracle.w2a8(oracle.pack_i2s(T2), c.S, q, s, N, K)
+    assert np.array_equal(r2["acc"][:, 3], q.astype(np.int32).sum(axis=1))
+    assert np.array_equal(r2["acc"][:, 4], q[:, 200].astype(np.int32))
+    # sign flip negates exactly
+    rn = oracle.w2a8(oracle.pack_i2s(-c.T), c.S, q, s, N, K)
+    assert np.array_equal(rn["acc"], -base["acc"]) and np.array_equal(rn["y"], -base["y"])
+    # linearity when the sum stays ternary
+    mask = wl.rng_for(9).random(c.T.shape) < 0.5
+    T_a = np.where(mask, c.T, 0).astype(np.int8)
+    T_b = np.where(mask, 0, c.T).astype(np.int8)
+    ra = oracle.w2a8(oracle.pack_i2s(T_a), c.S, q, s, N, K)
+    rb = oracle.w2a8(oracle.pack_i2s(T_b), c.S, q, s, N, K)
+    assert np.array_equal(ra["acc"] + rb["acc"], base["acc"])
+    # token independence (batch rows are independent)
+    r1 = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q[1:2], s[1:2], N, K)
+    assert np.array_equal(r1["acc"][0], base["acc"][1]) and np.array_equal(r1["y"][0], base["y"][1])
+
+
+# --------------------------------------------------------------------------- #
+# scale epilogue
+# --------------------------------------------------------------------------- #
+def test_scale_unit_scales_exact():
+    M, N, K = 4, 64, 1024
+    c = wl.small_case(2, M, N, K, skind="ones")
+    q, _ = oracle.quant_act_bf16(c.x_bits)
+    ones = np.ones(M, np.float32)
+    r = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, ones, N, K)
+    assert np.array_equal(r["y"], r["acc"].astype(np.float32))
+
+
+def test_scale_power_of_two_scaling():
+    M, N, K = 2, 32, 768
+    c = wl.small_case(3, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    P = oracle.pack_i2s(c.T)
+    r = oracle.w2a8(P, c.S, q, s, N, K)
+    r2 = oracle.w2a8(P, (c.S * 2).astype(np.float32), q, s, N, K)
+    r3 = oracle.w2a8(P, c.S, q, (s * 4).astype(np.float32), N, K)
+    assert np.array_equal(r2["y"], r["y"] * 2)
+    assert np.array_equal(r3["y"], r["y"] * 4)
+
+
+def test_scale_block_index_closed_form():
+    # one nonzero weight per row, in a different block per row: y = s_a * S[n,b] * t * q[k]
+    M, N, K = 2, 16, 1024
+    B = K // 128
+    rng = wl.rng_for(21)
+    S = rng.uniform(0.5, 2.0, size=(N, B)).astype(np.float32)
+    T = np.zeros((N, K), np.int8)
+    ks = []
+    for n in range(N):
+        k = int(rng.integers(0, K))
+        T[n, k] = 1 if n % 2 else -1
+        ks.append(k)
+    xb = wl.normal_act(rng, M, K)
+    q, s = oracle.quant_act_bf16(xb)
+    r = oracle.w2a8(oracle.pack_i2s(T), S, q, s, N, K)
+    for m in range(M):
+        for n in range(N):
+            k = ks[n]
+            exact = Fraction(float(s[m])) * Fraction(float(S[n, k // 128])) * int(T[n, k]) * int(q[m, k])
+            assert abs(Fraction(r["y64"][m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+            assert r["acc"][m, n] == int(T[n, k]) * int(q[m, k])
+
+
+def test_scale_magnitude_bounds_value():
+    c = wl.small_case(4, 4, 64, 1280)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    r = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, s, c.N, c.K)
+    assert np.all(np.abs(r["y64"]) <= r["mag"] * (1 + 1e-12))
+    assert np.array_equal(r["y"], r["y64"].astype(np.float32))
+
+
+# --------------------------------------------------------------------------- #
+# absmean ternarisation
+# --------------------------------------------------------------------------- #
+def test_ternarize_recovers_scaled_ternary():
+    rng = wl.rng_for(31)
+    N, K = 32, 512
+    T = wl.ternary_uniform(rng, N, K)
+    T[:, ::128] = 1  # at least one nonzero per block
+    c = np.float32(0.0371)
+    T2, S = oracle.ternarize_absmean(T.astype(np.float32) * c)
+    assert np.array_equal(T2, T)
+    nnz = np.abs(T.reshape(N, K // 128, 128)).sum(axis=2)
+    exact = (Fraction(float(c)) * nnz.astype(object)) / 128
+    for n in range(N):
+        for b in range(K // 128):
+            assert S[n, b] == np.float32(float(exact[n, b]))
+
+
+def test_ternarize_gaussian_zero_fraction_and_symmetry():
+    W = wl.normal_weights(wl.rng_for(32), 2048, 1280, 0.02)
+    T, S = oracle.ternarize_absmean(W)
+    # |W|/gamma < 1/2 with gamma ~ E|W| = sigma*sqrt(2/pi): P(|Z| < sqrt(2/pi)/2) = 0.3101
+    zf = float((T == 0).mean())
+    assert abs(zf - 0.3101) < 0.01, zf
+    assert abs(float((T == 1).mean()) - float((T == -1).mean())) < 0.005
+    Tn, Sn = oracle.ternarize_absmean(-W)
+    assert np.array_equal(Tn, -T) and np.array_equal(Sn, S)
+    # scale is the block mean of |W| (exact rational mean, rounded once)
+    blk = np.abs(W[:4, :128].astype(np.float64))
+    for n in range(4):
+        exact = sum(Fraction(float(v)) for v in blk[n]) / 128
+        assert abs(Fraction(float(S[n, 0])) - exact) <= exact * Fraction(1, 2 ** 24)
+
+
+def test_ternarize_zero_block_and_threshold():
+    W = np.zeros((2, 256), np.float32)
+    W[1, 128:] = 1.0
+    W[1, 130] = 0.49  # gamma = (127 + 0.49)/128 < 1 -> ratio 0.49/gamma < 0.5 -> 0
+    T, S = oracle.ternarize_absmean(W)
+    assert np.all(T[0] == 0) and np.all(S[0] == 0) and np.all(T[1, :128] == 0) and S[1, 0] == 0
+    assert T[1, 130] == 0 and T[1, 129] == 1
+
+
+# --------------------------------------------------------------------------- #
+# bf16 rounding and the chain junction
+# --------------------------------------------------------------------------- #
+def test_bf16_rne_points():
+    one = 1.0
+    ulp = 2.0 ** -7  # bf16 ulp at 1
+    vals = np.array([one, one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 2 ** -20, -2.5, 65280.0],
+                    np.float32)
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x477F]
+    assert list(oracle.f32_to_bf16(vals)) == want
+
+
+def test_fold_quant_closed_form():
+    H = 256
+    y = np.zeros((1, 2 * H), np.float32)
+    y[0, 3] = 1.0
+    y[0, H + 3] = 2.0  # h[3] = 3 = amax
+    y[0, 10] = -1.5
+    y[0, H + 10] = 0.0
+    q, s = oracle.fold_quant(y)
+    assert q[0, 3] == 127 and q[0, 10] == int(np.rint(np.float32(-1.5) * (np.float32(127) / np.float32(3))))
+    assert s[0] == np.float32(np.float32(3.0) / np.float32(127))
+    assert np.count_nonzero(q) == 2
