@@ -1,0 +1,268 @@
+"""Python binding of libbitnet_w2a8.so (MI355X / gfx950 W2A8 ternary product).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels or, for the offline packer, in its host C++ code.  torch supplies
+device memory and streams.  The C ABI and the tile layout are specified in
+``include/bitnet_w2a8.h``; the functions below carry the same names.
+
+If the library is not built, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitnet_w2a8.so")
+
+BITNET_OK, BITNET_ERR_INVALID_ARG, BITNET_ERR_UNSUPPORTED_SHAPE, BITNET_ERR_HIP = 0, 1, 2, 3
+BITNET_DT_BF16, BITNET_DT_F32 = 0, 1
+BLOCK_K = 128
+TILE_N = 16
+GEMV_MAX_M = 16
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {bitnet_status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+_SIGS = {
+    "bitnet_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "bitnet_check_shape": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
+    "bitnet_packed_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
+    "bitnet_scale_count": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
+    "bitnet_ternarize_absmean": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p], ctypes.c_int),
+    "bitnet_pack_i2s": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                         ctypes.c_void_p], ctypes.c_int),
+    "bitnet_repack_i2s": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                           ctypes.c_void_p], ctypes.c_int),
+    "bitnet_unpack_i2s": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                           ctypes.c_void_p], ctypes.c_int),
+    "bitnet_quant_act": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_quant_act_fold": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemv": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemm": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_acc_i32": ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
+}
+
+
+def lib():
+    """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run `python -m bit_gemv_i2_amd.build`)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _ok(status: int, what: str):
+    if status != BITNET_OK:
+        raise BitnetError(status, what)
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ sizes
+def bitnet_status_str(status: int) -> str:
+    return lib().bitnet_status_str(int(status)).decode()
+
+
+def bitnet_check_shape(N: int, K: int) -> int:
+    return lib().bitnet_check_shape(N, K)
+
+
+def bitnet_packed_bytes(N: int, K: int) -> int:
+    return lib().bitnet_packed_bytes(N, K)
+
+
+def bitnet_scale_count(N: int, K: int) -> int:
+    return lib().bitnet_scale_count(N, K)
+
+
+# ------------------------------------------------------------------ offline, host
+def bitnet_ternarize_absmean(w: np.ndarray):
+    """fp32 [N][K] -> (ternary int8 [N][K], scales fp32 [N][K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    t = np.empty((N, K), np.int8)
+    s = np.empty((N, K // BLOCK_K), np.float32)
+    _ok(lib().bitnet_ternarize_absmean(_np_ptr(w), N, K, _np_ptr(t), _np_ptr(s)), "bitnet_ternarize_absmean")
+    return t, s
+
+
+def bitnet_pack_i2s(ternary: np.ndarray, scales: np.ndarray):
+    """ternary int8 [N][K], scales fp32 [N][K/128] -> (packed uint8 [N*K/4], tiled scales fp32 [N*K/128])."""
+    ternary = np.ascontiguousarray(ternary, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    N, K = ternary.shape
+    if scales.shape != (N, K // BLOCK_K):
+        raise ValueError("scales must be [N][K/128]")
+    nb = bitnet_packed_bytes(N, K)
+    if nb == 0:
+        raise BitnetError(BITNET_ERR_UNSUPPORTED_SHAPE, "bitnet_pack_i2s")
+    packed = np.empty(nb, np.uint8)
+    st = np.empty(bitnet_scale_count(N, K), np.float32)
+    _ok(lib().bitnet_pack_i2s(_np_ptr(ternary), _np_ptr(scales), N, K, _np_ptr(packed), _np_ptr(st)),
+        "bitnet_pack_i2s")
+    return packed, st
+
+
+def bitnet_repack_i2s(i2s: np.ndarray, scales: np.ndarray, K: int):
+    """canonical i2_s bytes uint8 [N][K/4] + scales [N][K/128] -> (packed, tiled scales)."""
+    i2s = np.ascontiguousarray(i2s, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    N = i2s.shape[0]
+    if i2s.shape != (N, K // 4) or scales.shape != (N, K // BLOCK_K):
+        raise ValueError("bad i2s / scales shape")
+    nb = bitnet_packed_bytes(N, K)
+    if nb == 0:
+        raise BitnetError(BITNET_ERR_UNSUPPORTED_SHAPE, "bitnet_repack_i2s")
+    packed = np.empty(nb, np.uint8)
+    st = np.empty(bitnet_scale_count(N, K), np.float32)
+    _ok(lib().bitnet_repack_i2s(_np_ptr(i2s), _np_ptr(scales), N, K, _np_ptr(packed), _np_ptr(st)),
+        "bitnet_repack_i2s")
+    return packed, st
+
+
+def bitnet_unpack_i2s(packed: np.ndarray, scales_tiled: np.ndarray | None, N: int, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    t = np.empty((N, K), np.int8)
+    s = None
+    sp = None
+    if scales_tiled is not None:
+        scales_tiled = np.ascontiguousarray(scales_tiled, dtype=np.float32)
+        s = np.empty((N, K // BLOCK_K), np.float32)
+        sp = _np_ptr(scales_tiled)
+    _ok(lib().bitnet_unpack_i2s(_np_ptr(packed), sp, N, K, _np_ptr(t), None if s is None else _np_ptr(s)),
+        "bitnet_unpack_i2s")
+    return t, s
+
+
+# ------------------------------------------------------------------ device, async
+def bitnet_quant_act(x, q=None, s_a=None, stream=None):
+    """x: device [M][K] bf16 or fp32 -> (q int8 [M][K], s_a fp32 [M])."""
+    import torch
+    M, K = x.shape
+    xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
+    if xdt is None:
+        raise ValueError("x must be bf16 or fp32")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _ok(lib().bitnet_quant_act(_dev_ptr(x, "x"), xdt, M, K, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"),
+                               _stream(stream)), "bitnet_quant_act")
+    return q, s_a
+
+
+def bitnet_quant_act_fold(y, q=None, s_a=None, stream=None):
+    """y: device fp32 [M][2H] -> h = y[:, :H] + y[:, H:] quantised: (q int8 [M][H], s_a fp32 [M])."""
+    import torch
+    M, H2 = y.shape
+    H = H2 // 2
+    if y.dtype != torch.float32 or H2 % 2:
+        raise ValueError("y must be fp32 [M][2H]")
+    if q is None:
+        q = torch.empty((M, H), dtype=torch.int8, device=y.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=y.device)
+    _ok(lib().bitnet_quant_act_fold(_dev_ptr(y, "y"), M, H, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"),
+                                    _stream(stream)), "bitnet_quant_act_fold")
+    return q, s_a
+
+
+def bitnet_w2a8_gemv(packed, scales, q, s_a, N: int, K: int, y=None, stream=None):
+    """Decode product (M <= 16): y fp32 [M][N]."""
+    import torch
+    M = q.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    _ok(lib().bitnet_w2a8_gemv(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
+                               _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), M, N, K, _stream(stream)),
+        "bitnet_w2a8_gemv")
+    return y
+
+
+def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=None, stream=None):
+    """Prefill product (any M): y [M][N] in bf16 (default) or fp32."""
+    import torch
+    M = q.shape[0]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if y is None else y.dtype
+    ydt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(out_dtype)
+    if ydt is None:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    _ok(lib().bitnet_w2a8_gemm(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
+                               _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), ydt, M, N, K, _stream(stream)),
+        "bitnet_w2a8_gemm")
+    return y
+
+
+def bitnet_w2a8_acc_i32(packed, q, N: int, K: int, acc=None, stream=None):
+    """Exact int32 product acc [M][N] through the decode (M <= 16) or prefill kernel."""
+    import torch
+    M = q.shape[0]
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
+    _ok(lib().bitnet_w2a8_acc_i32(_dev_ptr(packed, "packed"), _dev_ptr(q, "q"), _dev_ptr(acc, "acc"), M, N, K,
+                                  _stream(stream)), "bitnet_w2a8_acc_i32")
+    return acc
+
+
+# ------------------------------------------------------------------ convenience
+@dataclass
+class PackedWeight:
+    """A ternary weight matrix resident in device memory in the tile layout."""
+    packed: object   # torch uint8 [N*K/4] on device
+    scales: object   # torch fp32 [N*K/128] on device (tiled order)
+    N: int
+    K: int
+
+    @classmethod
+    def from_ternary(cls, ternary: np.ndarray, scales: np.ndarray, device="cuda"):
+        import torch
+        p, s = bitnet_pack_i2s(ternary, scales)
+        N, K = ternary.shape
+        return cls(torch.from_numpy(p).to(device), torch.from_numpy(s).to(device), N, K)
+
+    def gemv(self, q, s_a, y=None, stream=None):
+        return bitnet_w2a8_gemv(self.packed, self.scales, q, s_a, self.N, self.K, y=y, stream=stream)
+
+    def gemm(self, q, s_a, out_dtype=None, y=None, stream=None):
+        return bitnet_w2a8_gemm(self.packed, self.scales, q, s_a, self.N, self.K, out_dtype=out_dtype, y=y,
+                                stream=stream)

@@ -1,0 +1,174 @@
+/*
+ * bitnet_w2a8.h -- C ABI of the MI355X (gfx950) W2A8 ternary product library.
+ *
+ * The operation (BitNet b1.58 linear layer, "W2A8"):
+ *   weights T[N][K] in {-1,0,+1} with one fp32 scale S[n][b] per 128-weight
+ *   block b of a row, activations quantised per token to int8 Q[M][K] with a
+ *   dequantisation factor s_a[m], and
+ *       y[m][n] = s_a[m] * sum_b S[n][b] * sum_{k in block b} T[n][k] * Q[m][k]
+ *   with the inner sums exact in int32.
+ * Sources (page, section):
+ *   [P2] "5x performance leap: BitNet vs llama.cpp 1-bit LLM inference" --
+ *        "Architecture foundations", item 2: a W2A8 GEMV (2-bit weights x
+ *        8-bit activations); "GPU kernel breakthroughs": offline weight
+ *        reordering for memory access, 8-bit dot products, and an
+ *        interleaved 16-codes-per-32-bit-word order that makes decoding cheap.
+ *   [P3] "Running 1-bit LLMs in the browser: BitNet + WebAssembly" --
+ *        "Why WASM": ternary weights from absmean quantisation;
+ *        "What i2_s actually is": code 0/1/2 for -1/0/+1, four codes per byte,
+ *        128-weight blocks with one float scale each.
+ *   [P4] "BitRun v0.2 measured" -- "Matrix memory bounds and stride safety":
+ *        packed rows must have one stride rule shared by reader and kernel;
+ *        here bitnet_packed_bytes() is that single authority.
+ *
+ * Conventions for every entry point
+ *   - Return value: bitnet_status_t.  Arguments are validated synchronously,
+ *     before any HIP call; an invalid call returns an error and launches
+ *     nothing.  Device entry points enqueue work on `stream` and return
+ *     without synchronising; a launch failure is reported as BITNET_ERR_HIP.
+ *     No C++ exception crosses this interface.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     memory, keeps no state between calls and is re-entrant.
+ *   - "device" pointers are HIP device memory, 16-byte aligned; "host"
+ *     pointers are ordinary host memory.  Non-finite inputs are outside the
+ *     contract.
+ *   - Shapes: K % 128 == 0 (blocks never straddle rows), N % 16 == 0,
+ *     N, K >= the block/tile size, and N*K < 2^40.
+ *
+ * gfx950 tile layout of packed weights ("packed", N*K/4 bytes)
+ *   Rows are grouped in tiles of 16 (T = n / 16), K in blocks of 128
+ *   (b = k / 128).  Brick (T, b) is 512 bytes at byte offset
+ *   (T * (K/128) + b) * 512.  Slot l = 16*g + j (g in 0..3, j in 0..15) of a
+ *   brick is 8 bytes at offset 8*l: two little-endian 32-bit words w_s
+ *   (s = 0, 1) for row n = 16*T + j and the 16 weights starting at
+ *   k0 = 128*b + 64*s + 16*g.  Bits 8p+2i .. 8p+2i+1 of w_s (byte p, field i,
+ *   p, i in 0..3) hold weight k0 + 4*i + p as a 2-bit two's-complement code
+ *   (0 -> 0, +1 -> 1, -1 -> 3).  This puts the 16 codes one wavefront lane
+ *   needs for one int8 matrix-core step in one word, and one shift and one
+ *   mask turn field i of all four bytes into four consecutive int8 weights
+ *   (times 64) -- the same idea as the interleaved word order of [P2].
+ * Tiled scales ("scales_tiled", N*K/128 fp32): the scale of row 16*T + j,
+ *   block b sits at index (T * (K/128) + b) * 16 + j.
+ * Canonical i2_s bytes (interchange, [P3]; reading of the garbled shift):
+ *   row n occupies K/4 bytes; byte j (0..31) of block b holds weights
+ *   128b + 32g + j for g = 0..3 at bits (7-2g)..(6-2g), code = t + 1.
+ */
+#ifndef BITNET_W2A8_H
+#define BITNET_W2A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_ERR_INVALID_ARG = 1,       /* null / misaligned pointer, bad dtype, non-ternary input */
+    BITNET_ERR_UNSUPPORTED_SHAPE = 2, /* shape outside the rules above */
+    BITNET_ERR_HIP = 3                /* a HIP launch or runtime call failed */
+} bitnet_status_t;
+
+typedef enum { BITNET_DT_BF16 = 0, BITNET_DT_F32 = 1 } bitnet_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *bitnet_status_str(int status);
+
+/* Checks (N, K) against the shape rules; BITNET_OK or BITNET_ERR_UNSUPPORTED_SHAPE. */
+bitnet_status_t bitnet_check_shape(int64_t N, int64_t K);
+
+/* Bytes of a packed weight buffer, N*K/4 (the only size/stride authority);
+ * 0 if the shape is unsupported. */
+size_t bitnet_packed_bytes(int64_t N, int64_t K);
+
+/* Number of fp32 block scales, N*K/128; 0 if the shape is unsupported. */
+size_t bitnet_scale_count(int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------- offline, host */
+
+/* absmean ternarisation per 128-weight block ([P3] "Why WASM" names absmean;
+ * [P3] "What i2_s actually is" gives the 128-block float scale).  For every row
+ * n and block b: gamma = (sum of |w| over the block in fp64, in index order) /
+ * 128 rounded to fp32; t = clamp(rint(w / gamma), -1, 1) with the ratio an fp32
+ * division (round half to even); scale = gamma; gamma == 0 gives t = 0.
+ *   w        host, fp32 [N][K] row-major (in)
+ *   ternary  host, int8 [N][K] row-major (out), values in {-1,0,1}
+ *   scales   host, fp32 [N][K/128] row-major (out) */
+bitnet_status_t bitnet_ternarize_absmean(const float *w, int64_t N, int64_t K,
+                                         int8_t *ternary, float *scales);
+
+/* Packs a ternary matrix into the gfx950 tile layout (the offline reorder of
+ * [P2] "GPU kernel breakthroughs", re-designed for 64-wide wavefronts).
+ *   ternary       host, int8 [N][K] row-major, each value in {-1,0,1}
+ *                 (anything else -> BITNET_ERR_INVALID_ARG, nothing written)
+ *   scales        host, fp32 [N][K/128] row-major block scales
+ *   packed_out    host, bitnet_packed_bytes(N,K) bytes, tile layout
+ *   scales_out    host, bitnet_scale_count(N,K) fp32, tiled scale order */
+bitnet_status_t bitnet_pack_i2s(const int8_t *ternary, const float *scales, int64_t N, int64_t K,
+                                uint8_t *packed_out, float *scales_out);
+
+/* Same as bitnet_pack_i2s, reading canonical i2_s bytes (host, uint8
+ * [N][K/4], [P3] code map; code 3 -> BITNET_ERR_INVALID_ARG). */
+bitnet_status_t bitnet_repack_i2s(const uint8_t *i2s, const float *scales, int64_t N, int64_t K,
+                                  uint8_t *packed_out, float *scales_out);
+
+/* Inverse of bitnet_pack_i2s (host): tile layout -> ternary int8 [N][K] and
+ * row-major scales [N][K/128].  scales_tiled / scales_out may both be NULL. */
+bitnet_status_t bitnet_unpack_i2s(const uint8_t *packed, const float *scales_tiled, int64_t N, int64_t K,
+                                  int8_t *ternary_out, float *scales_out);
+
+/* ---------------------------------------------------------------- device, async */
+
+/* Per-token absmax int8 quantisation of activations ([P2] "Architecture
+ * foundations": 8-bit activations; the quantiser itself is a reading): per
+ * token m, amax = max_k |x|, amax_c = max(amax, 1e-5), inv = 127/amax_c (fp32,
+ * correctly rounded), q = clamp(rint(x * inv), -127, 127) (fp32 product, half to
+ * even), s_a[m] = amax_c / 127.
+ *   x    device, [M][K] row-major, dtype xdt (BITNET_DT_BF16 or BITNET_DT_F32)
+ *   q    device, int8 [M][K] (out)
+ *   s_a  device, fp32 [M] (out)
+ * Rules: M >= 1, K >= 1, K % 16 == 0. */
+bitnet_status_t bitnet_quant_act(const void *x, int xdt, int M, int K, int8_t *q, float *s_a,
+                                 hipStream_t stream);
+
+/* Junction of a stacked decode chain: h[m][j] = y[m][j] + y[m][H + j] (one fp32
+ * addition; fused gate+up output folded to the down-projection width), then
+ * quantised exactly as bitnet_quant_act does.
+ *   y    device, fp32 [M][2H];  q device int8 [M][H];  s_a device fp32 [M].
+ * Rules: M >= 1, H % 16 == 0. */
+bitnet_status_t bitnet_quant_act_fold(const float *y, int M, int H, int8_t *q, float *s_a,
+                                      hipStream_t stream);
+
+/* Decode product, batch 1..16 (the W2A8 GEMV of [P2] "Architecture
+ * foundations", item 2), on the gfx950 int8 matrix cores.
+ *   packed  device, tile layout, bitnet_packed_bytes(N,K) bytes
+ *   scales  device, tiled scales, bitnet_scale_count(N,K) fp32
+ *   q       device, int8 [M][K];  s_a device, fp32 [M]
+ *   y       device, fp32 [M][N] (out)
+ * Rules: 1 <= M <= 16 and the shape rules.  The fp32 epilogue's summation order
+ * is unspecified: y agrees with the exact value within 1e-5 of
+ * max(|y|, s_a * sum_b |S*A|). */
+bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q,
+                                 const float *s_a, float *y, int M, int N, int K, hipStream_t stream);
+
+/* Prefill product for any M >= 1 on the int8 matrix cores; y is [M][N] in
+ * dtype ydt (BITNET_DT_BF16: fp32 value rounded to nearest even; or
+ * BITNET_DT_F32).  Arguments otherwise as bitnet_w2a8_gemv. */
+bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, const int8_t *q,
+                                 const float *s_a, void *y, int ydt, int M, int N, int K,
+                                 hipStream_t stream);
+
+/* Exact integer product acc[m][n] = sum_k T[n][k] * Q[m][k] (int32, device, [M][N]),
+ * computed by the same kernels as the two products above (M <= 16: the decode
+ * kernel; larger M: the prefill kernel), so that their integer core can be
+ * checked bit for bit.  Rules: M >= 1 and the shape rules. */
+bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int32_t *acc,
+                                    int M, int N, int K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_W2A8_H */

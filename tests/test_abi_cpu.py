@@ -1,0 +1,166 @@
+"""CPU-only checks of the C ABI library: it loads, exports every symbol the
+header declares, its host-side offline code (ternarise / pack / repack /
+unpack) agrees with the oracle bit for bit, the tile layout matches the
+header's specification, and invalid calls are rejected before any HIP call
+(no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_gemv_i2_amd as bn
+import oracle
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(bitnet_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) >= 13
+    lib = bn.lib()
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings():
+    assert bn.bitnet_status_str(0) == "ok"
+    assert "invalid" in bn.bitnet_status_str(1)
+    assert "shape" in bn.bitnet_status_str(2)
+    assert "HIP" in bn.bitnet_status_str(3)
+    assert bn.bitnet_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K,ok", [(2560, 2560, True), (13824, 2560, True), (20480, 3200, True), (2560, 6912, True),
+                                    (16, 128, True), (8, 128, False), (2560, 2500, False), (24, 128, False),
+                                    (0, 128, False), (16, 0, False), (-16, 128, False)])
+def test_shape_rules_and_sizes(N, K, ok):
+    assert (bn.bitnet_check_shape(N, K) == bn.BITNET_OK) == ok
+    assert bn.bitnet_packed_bytes(N, K) == (N * K // 4 if ok else 0)
+    assert bn.bitnet_scale_count(N, K) == (N * K // 128 if ok else 0)
+
+
+# ------------------------------------------------------------------ host offline code vs oracle
+@pytest.mark.parametrize("seed,N,K", [(0, 16, 128), (1, 48, 384), (2, 2560, 2560), (3, 13824, 2560)])
+def test_ternarize_matches_oracle(seed, N, K):
+    W = wl.normal_weights(wl.rng_for(41, seed), N, K, 0.02)
+    W[0, :128] = 0.0  # a zero block
+    t_lib, s_lib = bn.bitnet_ternarize_absmean(W)
+    t_or, s_or = oracle.ternarize_absmean(W)
+    assert np.array_equal(t_lib, t_or)
+    assert np.array_equal(s_lib.view(np.uint32), s_or.view(np.uint32))
+
+
+def test_ternarize_config2_matches_oracle():
+    c = wl.config2()
+    t_lib, s_lib = bn.bitnet_ternarize_absmean(c.W)
+    t_or, s_or = oracle.ternarize_absmean(c.W)
+    assert np.array_equal(t_lib, t_or) and np.array_equal(s_lib, s_or)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 640), (2560, 2560), (2560, 6912), (20480, 3200)])
+def test_pack_unpack_roundtrip_and_repack_from_canonical(N, K):
+    r = wl.rng_for(43, N, K)
+    T = wl.ternary_uniform(r, N, K)
+    S = wl.uniform_scales(r, N, K)
+    packed, st = bn.bitnet_pack_i2s(T, S)
+    assert packed.size == N * K // 4 and st.size == N * K // 128
+    T2, S2 = bn.bitnet_unpack_i2s(packed, st, N, K)
+    assert np.array_equal(T2, T) and np.array_equal(S2, S)
+    # the oracle's canonical i2_s bytes repack to the identical tile buffer
+    packed2, st2 = bn.bitnet_repack_i2s(oracle.pack_i2s(T), S, K)
+    assert np.array_equal(packed2, packed) and np.array_equal(st2, st)
+
+
+def test_tile_layout_matches_header_spec():
+    # place single weights and check the byte/bit position the header specifies
+    N, K = 32, 256
+    nblk = K // 128
+    for (n, k, t) in [(0, 0, 1), (17, 130, -1), (31, 255, 1), (5, 64 + 16 * 3 + 4 * 2 + 1, -1), (16, 7, 1)]:
+        T = np.zeros((N, K), np.int8)
+        T[n, k] = t
+        packed, _ = bn.bitnet_pack_i2s(T, np.ones((N, nblk), np.float32))
+        Tt, j = divmod(n, 16)
+        b, r = divmod(k, 128)
+        s, r = divmod(r, 64)
+        g, e = divmod(r, 16)
+        i, p = divmod(e, 4)
+        byte = (Tt * nblk + b) * 512 + (16 * g + j) * 8 + 4 * s + p
+        want = np.zeros_like(packed)
+        want[byte] = (t & 3) << (2 * i)
+        assert np.array_equal(packed, want), (n, k)
+    # scales: row 16T+j, block b at (T*nblk + b)*16 + j
+    S = np.arange(N * nblk, dtype=np.float32).reshape(N, nblk)
+    _, st = bn.bitnet_pack_i2s(np.zeros((N, K), np.int8), S)
+    for n in range(N):
+        for b in range(nblk):
+            assert st[((n // 16) * nblk + b) * 16 + n % 16] == S[n, b]
+
+
+def test_pack_rejects_bad_input_without_writing():
+    T = np.zeros((16, 128), np.int8)
+    T[3, 3] = 2
+    with pytest.raises(bn.BitnetError) as ei:
+        bn.bitnet_pack_i2s(T, np.ones((16, 1), np.float32))
+    assert ei.value.status == bn.BITNET_ERR_INVALID_ARG
+    P = np.full((16, 32), 0x55, np.uint8)
+    P[2, 2] = 0xC0 | 0x15  # code 3 in group 0
+    with pytest.raises(bn.BitnetError):
+        bn.bitnet_repack_i2s(P, np.ones((16, 1), np.float32), 128)
+    with pytest.raises(bn.BitnetError) as ei:
+        bn.bitnet_pack_i2s(np.zeros((24, 128), np.int8), np.ones((24, 1), np.float32))
+
+
+# ------------------------------------------------------------------ validation before any HIP call
+_FAKE = ctypes.c_void_p(0x100000)       # aligned, non-null, never dereferenced
+_MIS = ctypes.c_void_p(0x100004)        # misaligned
+_NULL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("M,N,K,ptr,want", [
+    (0, 2560, 2560, _FAKE, bn.BITNET_ERR_UNSUPPORTED_SHAPE),
+    (17, 2560, 2560, _FAKE, bn.BITNET_ERR_UNSUPPORTED_SHAPE),
+    (1, 2560, 2500, _FAKE, bn.BITNET_ERR_UNSUPPORTED_SHAPE),
+    (1, 2568, 2560, _FAKE, bn.BITNET_ERR_UNSUPPORTED_SHAPE),
+    (1, 2560, 2560, _NULL, bn.BITNET_ERR_INVALID_ARG),
+    (1, 2560, 2560, _MIS, bn.BITNET_ERR_INVALID_ARG),
+])
+def test_gemv_validation(M, N, K, ptr, want):
+    st = bn.lib().bitnet_w2a8_gemv(ptr, _FAKE, _FAKE, _FAKE, _FAKE, M, N, K, _NULL)
+    assert st == want
+
+
+def test_gemm_acc_quant_validation():
+    L = bn.lib()
+    assert L.bitnet_w2a8_gemm(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 7, 4, 16, 128, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_gemm(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 0, 0, 16, 128, _NULL) == \
+        bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_w2a8_gemm(_FAKE, _FAKE, _MIS, _FAKE, _FAKE, 0, 4, 16, 128, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_acc_i32(_FAKE, _FAKE, _FAKE, 4, 16, 100, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_w2a8_acc_i32(_FAKE, _FAKE, _NULL, 4, 16, 128, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_quant_act(_FAKE, 5, 1, 256, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_quant_act(_FAKE, 0, 1, 250, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_quant_act(_FAKE, 0, 0, 256, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_quant_act(_MIS, 0, 1, 256, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_quant_act_fold(_FAKE, 1, 24, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_quant_act_fold(_NULL, 1, 32, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_fallback(monkeypatch):
+    # a missing library must raise, never compute on the CPU
+    monkeypatch.setattr(bn, "_lib", None)
+    monkeypatch.setattr(bn, "LIB_PATH", os.path.join(ROOT, "does_not_exist.so"))
+    with pytest.raises(RuntimeError):
+        bn.lib()

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars: int8 activations, dequant factors and int32 accumulators bit-exact;
+fp32 outputs within 1e-5 of max(|y|, mag) where mag = s_a * sum_b |S*A| (the
+epilogue's fp32 summation order is free; its worst-case rounding is about
+(blocks + waves) * 2^-24 * mag); bf16 outputs are a round-to-nearest-even of a
+value inside that band."""
+import numpy as np
+import pytest
+
+import bit_gemv_i2_amd as bn
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-5
+
+torch = pytest.importorskip("torch")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def x_dev(bits):
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pack_dev(T, S):
+    p, s = bn.bitnet_pack_i2s(T, S)
+    return dev(p), dev(s)
+
+
+def assert_f32_close(y, ref, what=""):
+    y64, mag = ref["y64"], ref["mag"]
+    bound = RTOL * np.maximum(np.abs(y64), mag)
+    err = np.abs(y.astype(np.float64) - y64)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} outside tolerance, worst {(err / np.maximum(bound, 1e-300)).max():.3g}x"
+
+
+def assert_bf16_ok(ybits, ref, what=""):
+    y64, mag = ref["y64"], ref["mag"]
+    tol = RTOL * np.maximum(np.abs(y64), mag)
+    lo = wl.bf16_to_f32(oracle.f32_to_bf16((y64 - tol).astype(np.float32))).astype(np.float64)
+    hi = wl.bf16_to_f32(oracle.f32_to_bf16((y64 + tol).astype(np.float32))).astype(np.float64)
+    yv = wl.bf16_to_f32(ybits).astype(np.float64)
+    bad = (yv < lo) | (yv > hi)
+    assert not bad.any(), f"{what}: {bad.sum()} bf16 outputs outside the rounding band"
+
+
+def oracle_ref(T, S, q, s_a):
+    N, K = T.shape
+    return oracle.w2a8(oracle.pack_i2s(T), S, q, s_a, N, K)
+
+
+# ------------------------------------------------------------------ MFMA operand layout (builtin check)
+def test_zz_layout_single_weight(gpu):
+    # one nonzero weight at a time, one nonzero activation: checks every index of the decode
+    N, K = 32, 256
+    for (n, k) in [(0, 0), (17, 130), (31, 255), (5, 64 + 48 + 9), (16, 7), (9, 127)]:
+        T = np.zeros((N, K), np.int8)
+        T[n, k] = -1
+        q = np.zeros((3, K), np.int8)
+        q[2, k] = 101
+        q[0, k] = -7
+        p, s = pack_dev(T, np.ones((N, K // 128), np.float32))
+        acc = host(bn.bitnet_w2a8_acc_i32(p, dev(q), N, K))
+        want = np.zeros((3, N), np.int32)
+        want[2, n] = -101
+        want[0, n] = 7
+        assert np.array_equal(acc, want), (n, k)
+
+
+# ------------------------------------------------------------------ activation quantisation
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_quant_bf16_configs_bitexact(gpu, cfg):
+    M = {1: 1, 2: 8, 3: 1, 4: 512}[cfg]
+    c = wl.CONFIGS[cfg](M=M)
+    q, s = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 2576), (7, 6912), (2, 4096 + 16)])
+def test_quant_f32_and_edge_bitexact(gpu, M, K):
+    r = wl.rng_for(51, M, K)
+    x = (r.standard_t(3, size=(M, K)) * 10.0 ** r.integers(-3, 4, size=(M, 1))).astype(np.float32)
+    x[0] = 0.0  # zero token -> q = 0, s_a = 1e-5/127
+    if M > 1:
+        x[1, ::7] = -x[1, ::7]
+    q, s = bn.bitnet_quant_act(dev(x))
+    qo, so = oracle.quant_act_f32(x)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    assert np.all(host(q)[0] == 0)
+
+
+@pytest.mark.parametrize("M,H", [(1, 6912), (8, 6912), (3, 48)])
+def test_quant_fold_bitexact(gpu, M, H):
+    y = wl.rng_for(52, M, H).standard_normal((M, 2 * H)).astype(np.float32) * 3
+    q, s = bn.bitnet_quant_act_fold(dev(y))
+    qo, so = oracle.fold_quant(y)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+
+
+# ------------------------------------------------------------------ exact integer core
+SMALL_SHAPES = [(16, 128), (48, 384), (80, 640), (272, 2688), (64, 8960), (2064, 128 * 3)]
+
+
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+def test_acc_i32_gemv_path_bitexact(gpu, M, N, K):
+    c = wl.small_case(M * 7 + N, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    p, st = pack_dev(c.T, c.S)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, dev(q), N, K))
+    assert np.array_equal(acc, oracle_ref(c.T, c.S, q, s)["acc"])
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 48, 384), (130, 272, 1280), (300, 160, 2560), (512, 16, 128)])
+def test_acc_i32_gemm_path_bitexact(gpu, M, N, K):
+    c = wl.small_case(M + N + K, M, N, K, wkind="sparse")
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    p, st = pack_dev(c.T, c.S)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, dev(q), N, K))
+    assert np.array_equal(acc, oracle_ref(c.T, c.S, q, s)["acc"])
+
+
+# ------------------------------------------------------------------ fp32 / bf16 products
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_gemv_small_within_tolerance(gpu, M, N, K):
+    c = wl.small_case(M * 11 + K, M, N, K, xkind="t3")
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    p, st = pack_dev(c.T, c.S)
+    y = host(bn.bitnet_w2a8_gemv(p, st, dev(q), dev(s), N, K))
+    assert_f32_close(y, oracle_ref(c.T, c.S, q, s), f"gemv {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 48, 384), (33, 272, 1280), (130, 160, 2688), (256, 144, 640)])
+@pytest.mark.parametrize("ydt", ["bf16", "f32"])
+def test_gemm_small_within_tolerance(gpu, M, N, K, ydt):
+    c = wl.small_case(M * 3 + N, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    p, st = pack_dev(c.T, c.S)
+    out = torch.bfloat16 if ydt == "bf16" else torch.float32
+    y = bn.bitnet_w2a8_gemm(p, st, dev(q), dev(s), N, K, out_dtype=out)
+    ref = oracle_ref(c.T, c.S, q, s)
+    if ydt == "bf16":
+        assert_bf16_ok(host(y.view(torch.int16)).view(np.uint16), ref, "gemm bf16")
+    else:
+        assert_f32_close(host(y), ref, "gemm f32")
+
+
+def test_zero_weights_and_zero_tokens(gpu):
+    M, N, K = 4, 64, 1024
+    c = wl.small_case(3, M, N, K)
+    x = wl.bf16_to_f32(c.x_bits)
+    x[2] = 0.0
+    q, s = bn.bitnet_quant_act(dev(x))
+    p, st = pack_dev(c.T, c.S)
+    y = host(bn.bitnet_w2a8_gemv(p, st, q, s, N, K))
+    assert np.all(y[2] == 0.0)
+    pz, sz = pack_dev(np.zeros((N, K), np.int8), c.S)
+    assert np.all(host(bn.bitnet_w2a8_gemv(pz, sz, q, s, N, K)) == 0.0)
+    assert np.all(host(bn.bitnet_w2a8_gemm(pz, sz, q, s, N, K, out_dtype=torch.float32)) == 0.0)
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _full_gemv(c, T, S, what):
+    # end to end on the device: bf16 activations -> quant -> product
+    qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    assert np.array_equal(host(qd), qo) and np.array_equal(host(sd), so)
+    p, st = pack_dev(T, S)
+    y = host(bn.bitnet_w2a8_gemv(p, st, qd, sd, c.N, c.K))
+    ref = oracle_ref(T, S, qo, so)
+    assert_f32_close(y, ref, what)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, c.N, c.K))
+    assert np.array_equal(acc, ref["acc"])
+
+
+@pytest.mark.slow
+def test_config1_gemv_full(gpu):
+    c = wl.config1()
+    _full_gemv(c, c.T, c.S, "config1")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1, 8])
+def test_config2_gemv_full(gpu, M):
+    c = wl.config2(M=M)
+    T, S = bn.bitnet_ternarize_absmean(c.W)
+    To, So = oracle.ternarize_absmean(c.W)
+    assert np.array_equal(T, To) and np.array_equal(S, So)
+    _full_gemv(c, T, S, f"config2 M={M}")
+
+
+@pytest.mark.slow
+def test_config3_gemv_full(gpu):
+    c = wl.config3()
+    _full_gemv(c, c.T, c.S, "config3")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [0, 4, 5])
+@pytest.mark.parametrize("M", [1, 8])
+def test_stack_shapes_gemv_full(gpu, idx, M):
+    T, S = wl.stack_matrix(0, idx)
+    N, K = T.shape
+    xb = wl.normal_act(wl.rng_for(53, idx, M), M, K)
+    c = wl.Case(f"stack{idx}", M, N, K, x_bits=xb)
+    _full_gemv(c, T, S, f"stack matrix {idx} M={M}")
+
+
+@pytest.mark.slow
+def test_config4_gemm_full_sampled(gpu):
+    c = wl.config4()
+    qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    assert np.array_equal(host(qd), qo) and np.array_equal(host(sd), so)
+    p, st = pack_dev(c.T, c.S)
+    y = bn.bitnet_w2a8_gemm(p, st, qd, sd, c.N, c.K)
+    ybits = host(y.view(torch.int16)).view(np.uint16)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, c.N, c.K))
+    r = wl.rng_for(54)
+    toks = np.sort(r.choice(c.M, 48, replace=False))
+    toks[0], toks[-1] = 0, c.M - 1
+    rows = np.sort(r.choice(c.N, 640, replace=False))
+    rows[0], rows[-1] = 0, c.N - 1
+    ref = oracle.w2a8(oracle.pack_i2s(c.T[rows]), c.S[rows], qo[toks], so[toks], len(rows), c.K)
+    assert np.array_equal(acc[np.ix_(toks, rows)], ref["acc"])
+    assert_bf16_ok(ybits[np.ix_(toks, rows)], ref, "config4 sampled")
