@@ -70,103 +70,132 @@ class Rotation:
         return self.packed[i % self.R], self.scales[i % self.R]
 
 
-def time_per_launch(torch, launch, n, stream):
-    """Runs launch(i) n times on `stream`, each bracketed by a pair of events.
-    Returns (total_ms, per-launch ms array)."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+def capture(torch, launch, n):
+    """Captures launch(0..n-1) (each enqueuing on the current stream) into one HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(n, 4)):
+            launch(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            launch(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Replays g reps times between two events on the current stream; returns total ms."""
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def graph_us_per_launch(torch, launch, n, reps):
+    g = capture(torch, launch, n)
+    return time_graph(torch, g, reps) * 1e3 / (n * reps)
+
+
+def eager_us_per_launch(torch, launch, n):
+    stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(n):
-        ev[i][0].record(stream)
-        launch(i)
-        ev[i][1].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1), np.array([a.elapsed_time(b) for a, b in ev])
-
-
-def time_loop(torch, launch, n, stream):
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(n):
         launch(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / n
+    return t0.elapsed_time(t1) * 1e3 / n
 
 
 # ----------------------------------------------------------------------------
-def decode_shape(torch, bn, wl, name, N, K, M, T, S, xbits, iters, warmup, stream):
-    """Per-launch timing of quant + product for one decode shape."""
-    packed, st = bn.bitnet_pack_i2s(T, S)
-    rot = Rotation(torch, packed, st)
-    x = torch.from_numpy(xbits.view(np.int16)).cuda().view(torch.bfloat16)
-    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
-    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
-    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+class DecodeShape:
+    """Device buffers of one decode workload: a rotation of packed weights,
+    bf16 activations, int8/scale scratch and fp32 outputs."""
 
-    def step(i):
-        bn.bitnet_quant_act(x, q, sa, stream=stream)
-        p, s = rot[i]
-        bn.bitnet_w2a8_gemv(p, s, q, sa, N, K, y=y, stream=stream)
+    def __init__(self, torch, bn, name, N, K, M, T, S, xbits):
+        self.torch, self.bn, self.name, self.N, self.K, self.M = torch, bn, name, N, K, M
+        packed, st = bn.bitnet_pack_i2s(T, S)
+        self.rot = Rotation(torch, packed, st)
+        self.packed_bytes = packed.nbytes
+        self.x = torch.from_numpy(xbits.view(np.int16)).cuda().view(torch.bfloat16)
+        self.q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        self.sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-    def gemv_only(i):
-        p, s = rot[i]
-        bn.bitnet_w2a8_gemv(p, s, q, sa, N, K, y=y, stream=stream)
+    def quant(self, i):
+        self.bn.bitnet_quant_act(self.x, self.q, self.sa)
 
-    for i in range(warmup):
-        step(i)
-    step_ms = time_loop(torch, step, iters, stream)
-    _, per = time_per_launch(torch, gemv_only, iters, stream)
-    loop_ms = time_loop(torch, gemv_only, iters, stream)
-    kern_ms = float(np.mean(per))
-    pb = N * K // 4
-    ab = gemv_bytes(M, N, K)
-    return {
-        "shape": name, "M": M, "N": N, "K": K, "rotation_copies": rot.R,
-        "step_us": step_ms * 1e3,
-        "gemv_event_us_mean": kern_ms * 1e3, "gemv_event_us_median": float(np.median(per)) * 1e3,
-        "gemv_event_us_min": float(np.min(per)) * 1e3,
-        "gemv_loop_us": loop_ms * 1e3,
-        "packed_GBps_step": pb / (step_ms * 1e-3) / 1e9,
-        "packed_GBps_gemv": pb / (kern_ms * 1e-3) / 1e9,
-        "packed_pct_hbm_gemv": 100.0 * pb / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "alg_GBps_gemv": ab / (kern_ms * 1e-3) / 1e9,
-        "alg_bytes": ab,
-    }
+    def gemv(self, i):
+        p, s = self.rot[i]
+        self.bn.bitnet_w2a8_gemv(p, s, self.q, self.sa, self.N, self.K, y=self.y)
+
+    def step2(self, i):
+        """Two launches: quantise, then multiply."""
+        self.quant(i)
+        self.gemv(i)
+
+    def fused(self, i):
+        """One launch: quantise-and-multiply."""
+        p, s = self.rot[i]
+        self.bn.bitnet_w2a8_gemv_act(p, s, self.x, self.N, self.K, y=self.y)
+
+    def measure(self, reps=20):
+        torch = self.torch
+        n = self.rot.R
+        step2_us = graph_us_per_launch(torch, self.step2, n, reps)
+        fused_us = graph_us_per_launch(torch, self.fused, n, reps)
+        gemv_us = graph_us_per_launch(torch, self.gemv, n, reps)
+        quant_us = graph_us_per_launch(torch, self.quant, 64, reps)
+        pb = self.packed_bytes
+        ab = gemv_bytes(self.M, self.N, self.K)
+        best = min(step2_us, fused_us)
+        return {
+            "shape": self.name, "M": self.M, "N": self.N, "K": self.K, "rotation_copies": n,
+            "step_us": best, "step_two_launch_us": step2_us, "step_fused_us": fused_us,
+            "gemv_us": gemv_us, "quant_us": quant_us,
+            "packed_GBps_step": pb / best / 1e3, "packed_GBps_gemv": pb / gemv_us / 1e3,
+            "packed_pct_hbm_gemv": 100.0 * pb / gemv_us / 1e3 / HBM_PEAK_GBS,
+            "alg_GBps_gemv": ab / gemv_us / 1e3, "alg_bytes": ab,
+        }
 
 
-def prefill_shape(torch, bn, wl, iters, warmup, stream):
+def prefill_shape(torch, bn, wl, reps=10):
     c = wl.config4()
     packed, st = bn.bitnet_pack_i2s(c.T, c.S)
     p = torch.from_numpy(packed).cuda()
     s = torch.from_numpy(st).cuda()
     x = torch.from_numpy(c.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    q, sa = bn.bitnet_quant_act(x, stream=stream)
+    q, sa = bn.bitnet_quant_act(x)
     y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
 
     def gemm(i):
-        bn.bitnet_w2a8_gemm(p, s, q, sa, c.N, c.K, y=y, stream=stream)
+        bn.bitnet_w2a8_gemm(p, s, q, sa, c.N, c.K, y=y)
 
     def step(i):
-        bn.bitnet_quant_act(x, q, sa, stream=stream)
+        bn.bitnet_quant_act(x, q, sa)
         gemm(i)
 
-    for i in range(warmup):
-        step(i)
-    step_ms = time_loop(torch, step, iters, stream)
-    _, per = time_per_launch(torch, gemm, iters, stream)
-    kern_ms = float(np.mean(per))
+    gemm_us = graph_us_per_launch(torch, gemm, 20, reps)
+    step_us = graph_us_per_launch(torch, step, 20, reps)
     ops = 2.0 * c.M * c.N * c.K
     return {
         "shape": "gemm_512x13824x2560", "M": c.M, "N": c.N, "K": c.K,
-        "step_us": step_ms * 1e3, "gemm_event_us_mean": kern_ms * 1e3,
-        "int8_TOPS": ops / (kern_ms * 1e-3) / 1e12,
-        "int8_mfma_pct": 100.0 * ops / (kern_ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS,
+        "step_us": step_us, "gemm_us": gemm_us,
+        "int8_TOPS": ops / gemm_us / 1e6,
+        "int8_mfma_pct": 100.0 * ops / gemm_us / 1e6 / INT8_MFMA_PEAK_TOPS,
     }
 
 
@@ -219,56 +248,35 @@ def main():
     import workloads as wl
 
     bn.lib()  # fail loudly if the HIP library is missing
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    torch.cuda.set_device(0)
 
     # ---- headline workload: 13824x2560, M=1, absmean-ternarised N(0,0.02) weights
     c = wl.config2(M=1)
     T, S = bn.bitnet_ternarize_absmean(c.W)
     log(f"headline: 13824x2560 M=1, steps={args.steps} warmup={args.warmup}")
-    N, K, M = c.N, c.K, c.M
-    packed, st = bn.bitnet_pack_i2s(T, S)
-    rot = Rotation(torch, packed, st)
-    x = torch.from_numpy(c.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    q = torch.empty((M, K), dtype=torch.int8, device=dev)
-    sa = torch.empty((M,), dtype=torch.float32, device=dev)
-    y = torch.empty((M, N), dtype=torch.float32, device=dev)
-
-    gemv_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-
-    def step(i, timed=False):
-        bn.bitnet_quant_act(x, q, sa, stream=stream)
-        p, s = rot[i]
-        if timed:
-            gemv_ev[i][0].record(stream)
-        bn.bitnet_w2a8_gemv(p, s, q, sa, N, K, y=y, stream=stream)
-        if timed:
-            gemv_ev[i][1].record(stream)
-
+    d = DecodeShape(torch, bn, "gemv_13824x2560", c.N, c.K, c.M, T, S, c.x_bits)
     for i in range(args.warmup):
-        step(i)
+        d.fused(i)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i, timed=True)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    # exactly `steps` decode steps (one quantise-and-multiply launch each),
+    # captured once as a HIP graph and replayed
+    g = capture(torch, d.fused, args.steps)
+    total_ms = time_graph(torch, g, 1)
     ms_per_step = total_ms / args.steps
-    per = np.array([a.elapsed_time(b) for a, b in gemv_ev])
-    kern_ms = float(np.mean(per))
-    # a clean pass without the per-launch events, for reference
-    clean_ms = time_loop(torch, lambda i: step(i), args.steps, stream)
+    del g
+    # the product kernel alone (pre-quantised input): one graph over the weight rotation
+    reps = max(1, args.steps // d.rot.R)
+    gemv_us = graph_us_per_launch(torch, d.gemv, d.rot.R, reps)
+    quant_us = graph_us_per_launch(torch, d.quant, 64, 10)
+    step2_us = graph_us_per_launch(torch, d.step2, d.rot.R, reps)
+    eager_us = eager_us_per_launch(torch, d.fused, min(args.steps, 500))
 
+    N, K, M = c.N, c.K, c.M
     pbytes = N * K // 4
     ab = gemv_bytes(M, N, K)
-    achieved = ab / (kern_ms * 1e-3) / 1e9
+    achieved = ab / gemv_us / 1e3
     result = {
-        "metric": "W2A8 GEMV packed-weight GB/s, 13824x2560 batch 1 (quant + product per step)",
+        "metric": "W2A8 GEMV packed-weight GB/s, 13824x2560 batch 1 (quantise + product per step)",
         "value": pbytes / (ms_per_step * 1e-3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
@@ -278,26 +286,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xternary->int32, fp32 epilogue",
+        "dtype": "int8 x ternary -> int32, fp32 epilogue",
         "data": "synthetic (seeded; absmean-ternarised N(0,0.02) weights, N(0,1) bf16 activations)",
         "config": {"workload": "gemv_13824x2560_m1", "M": M, "N": N, "K": K,
-                   "rotation_copies": rot.R, "rotation_bytes": rot.R * (packed.nbytes + st.nbytes)},
+                   "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32)},
         "step_us": ms_per_step * 1e3,
-        "step_us_without_events": clean_ms * 1e3,
-        "pct_hbm_packed": 100.0 * pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "pct_hbm_packed_step": 100.0 * pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "quant_us": quant_us,
+        "step_two_launch_us": step2_us,
+        "eager_step_us": eager_us,
         "roofline": {
             "bound": "hbm", "kernel": "gemv_kernel (bitnet_w2a8_gemv)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None, "alg_bytes_per_launch": ab,
-            "kernel_us_mean": kern_ms * 1e3, "kernel_us_median": float(np.median(per)) * 1e3,
+            "traffic": None, "alg_bytes_per_launch": ab, "kernel_us": gemv_us,
+            "packed_GBps_kernel": pbytes / gemv_us / 1e3,
         },
     }
-    log(f"headline: {ms_per_step * 1e3:.2f} us/step, gemv {kern_ms * 1e3:.2f} us, "
-        f"{result['value']:.0f} GB/s packed per step")
+    log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
+        f"gemv {gemv_us:.2f} us, quant {quant_us:.2f} us, two-launch step {step2_us:.2f} us, "
+        f"eager step {eager_us:.2f} us")
+    del d
+    torch.cuda.empty_cache()
 
     if not args.quick:
         shapes = []
-        iters = max(200, min(2000, args.steps))
         for name, cfg, Ms in [("gemv_2560x2560", 1, [1]), ("gemv_13824x2560", 2, [1, 8]),
                               ("gemv_20480x3200", 3, [1])]:
             for Mi in Ms:
@@ -306,15 +318,20 @@ def main():
                     Tt, Ss = bn.bitnet_ternarize_absmean(cc.W)
                 else:
                     Tt, Ss = cc.T, cc.S
-                r = decode_shape(torch, bn, wl, name, cc.N, cc.K, Mi, Tt, Ss, cc.x_bits, iters, 50, stream)
+                ds = DecodeShape(torch, bn, name, cc.N, cc.K, Mi, Tt, Ss, cc.x_bits)
+                r = ds.measure()
+                del ds
+                torch.cuda.empty_cache()
                 log(json.dumps(r))
                 shapes.append(r)
         T5, S5 = wl.stack_matrix(0, 5)
-        r = decode_shape(torch, bn, wl, "gemv_2560x6912", 2560, 6912, 1, T5, S5,
-                         wl.normal_act(wl.rng_for(5, 99), 1, 6912), iters, 50, stream)
+        ds = DecodeShape(torch, bn, "gemv_2560x6912", 2560, 6912, 1, T5, S5,
+                         wl.normal_act(wl.rng_for(5, 99), 1, 6912))
+        r = ds.measure()
+        del ds
         log(json.dumps(r))
         shapes.append(r)
-        r = prefill_shape(torch, bn, wl, 200, 20, stream)
+        r = prefill_shape(torch, bn, wl)
         log(json.dumps(r))
         shapes.append(r)
         result["shapes"] = shapes

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitnet_w2a8.so")
 
 BITNET_OK, BITNET_ERR_INVALID_ARG, BITNET_ERR_UNSUPPORTED_SHAPE, BITNET_ERR_HIP = 0, 1, 2, 3
-BITNET_DT_BF16, BITNET_DT_F32 = 0, 1
+BITNET_DT_BF16, BITNET_DT_F32, BITNET_DT_F32_FOLD2 = 0, 1, 2
 BLOCK_K = 128
 TILE_N = 16
 GEMV_MAX_M = 16
@@ -52,6 +52,8 @@ _SIGS = {
                                ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemv": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemm": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemv_act": ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3
+                             + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_acc_i32": ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
 }
 
@@ -216,6 +218,30 @@ def bitnet_w2a8_gemv(packed, scales, q, s_a, N: int, K: int, y=None, stream=None
     return y
 
 
+def bitnet_w2a8_gemv_act(packed, scales, x, N: int, K: int, fold: bool = False, y=None, q_out=None,
+                         s_a_out=None, stream=None):
+    """Decode step in one launch: quantise x (bf16/fp32 [M][K], or fp32 [M][2K]
+    folded when fold=True) and multiply.  Optional q_out / s_a_out receive the
+    int8 activations and dequant factors.  Returns y fp32 [M][N]."""
+    import torch
+    M = x.shape[0]
+    if fold:
+        if x.dtype != torch.float32 or x.shape[1] != 2 * K:
+            raise ValueError("fold needs fp32 x of shape [M][2K]")
+        xdt = BITNET_DT_F32_FOLD2
+    else:
+        xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
+        if xdt is None or x.shape[1] != K:
+            raise ValueError("x must be bf16 or fp32 [M][K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    qp = None if q_out is None else _dev_ptr(q_out, "q_out")
+    sp = None if s_a_out is None else _dev_ptr(s_a_out, "s_a_out")
+    _ok(lib().bitnet_w2a8_gemv_act(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"), xdt,
+                                   _dev_ptr(y, "y"), qp, sp, M, N, K, _stream(stream)), "bitnet_w2a8_gemv_act")
+    return y
+
+
 def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=None, stream=None):
     """Prefill product (any M): y [M][N] in bf16 (default) or fp32."""
     import torch
@@ -262,6 +288,10 @@ class PackedWeight:
 
     def gemv(self, q, s_a, y=None, stream=None):
         return bitnet_w2a8_gemv(self.packed, self.scales, q, s_a, self.N, self.K, y=y, stream=stream)
+
+    def gemv_act(self, x, fold=False, y=None, q_out=None, s_a_out=None, stream=None):
+        return bitnet_w2a8_gemv_act(self.packed, self.scales, x, self.N, self.K, fold=fold, y=y, q_out=q_out,
+                                    s_a_out=s_a_out, stream=stream)
 
     def gemm(self, q, s_a, out_dtype=None, y=None, stream=None):
         return bitnet_w2a8_gemm(self.packed, self.scales, q, s_a, self.N, self.K, out_dtype=out_dtype, y=y,

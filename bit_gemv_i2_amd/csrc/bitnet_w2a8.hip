@@ -32,7 +32,6 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxGemvWaves = 16;
 constexpr int kGemvMaxM = 16;
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -56,57 +55,147 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 }
 
 // ==========================================================================
-// a4: per-token absmax int8 quantisation.  One workgroup of 256 threads per
-// token; each thread handles 8 consecutive values per step (16-byte loads for
-// bf16, 2x16 for fp32).  Pass 1 finds amax (exact, order-free), pass 2
-// quantises (the token is re-read from L2).
-// MODE 0: bf16 input; 1: fp32 input; 2: fp32 [M][2H] folded (h = lo + hi).
+// Activation sources.  XM 0: bf16 [M][K]; 1: fp32 [M][K]; 2: fp32 [M][2K]
+// folded, h = lo + hi (one fp32 addition, the junction of a stacked chain).
+// load8 reads values 8v .. 8v+7 of token m, widened exactly to fp32.
 // ==========================================================================
-template <int MODE>
-__device__ __forceinline__ void load8(const void *__restrict__ x, int m, int K, int v, float out[8]) {
-    if (MODE == 0) {
-        const uint4 u = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (size_t)m * K)[v];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// The raw 16-byte words behind 8 values (bf16: one, fp32: two, folded fp32: four),
+// so that loads can be issued early and converted only when their data is needed.
+template <int XM>
+struct Raw8 {
+    uint4 u[XM == 0 ? 1 : (XM == 1 ? 2 : 4)];
+};
+
+template <int XM>
+__device__ __forceinline__ Raw8<XM> load_raw8(const void *__restrict__ x, int m, int K, int v) {
+    Raw8<XM> r;
+    if constexpr (XM == 0) {
+        r.u[0] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (size_t)m * K)[v];
+    } else if constexpr (XM == 1) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + (size_t)m * K) + 2 * v;
+        r.u[0] = p[0];
+        r.u[1] = p[1];
+    } else {
+        const float *row = static_cast<const float *>(x) + (size_t)m * 2 * K;
+        const uint4 *lo = reinterpret_cast<const uint4 *>(row) + 2 * v;
+        const uint4 *hi = reinterpret_cast<const uint4 *>(row + K) + 2 * v;
+        r.u[0] = lo[0];
+        r.u[1] = lo[1];
+        r.u[2] = hi[0];
+        r.u[3] = hi[1];
+    }
+    return r;
+}
+
+__device__ __forceinline__ void words8(const uint4 &a, const uint4 &b, uint32_t w[8]) {
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <int XM>
+__device__ __forceinline__ void cvt8(const Raw8<XM> &r, float out[8]) {
+    if constexpr (XM == 0) {
+        const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             out[2 * i] = __uint_as_float(w[i] << 16);
             out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
-    } else if (MODE == 1) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (size_t)m * K) + 2 * v;
-        const float4 a = p[0], b = p[1];
-        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
     } else {
-        const float *row = static_cast<const float *>(x) + (size_t)m * 2 * K;
-        const float4 *lo = reinterpret_cast<const float4 *>(row) + 2 * v;
-        const float4 *hi = reinterpret_cast<const float4 *>(row + K) + 2 * v;
-        const float4 a = lo[0], b = lo[1], c = hi[0], d = hi[1];
-        out[0] = __fadd_rn(a.x, c.x); out[1] = __fadd_rn(a.y, c.y);
-        out[2] = __fadd_rn(a.z, c.z); out[3] = __fadd_rn(a.w, c.w);
-        out[4] = __fadd_rn(b.x, d.x); out[5] = __fadd_rn(b.y, d.y);
-        out[6] = __fadd_rn(b.z, d.z); out[7] = __fadd_rn(b.w, d.w);
+        uint32_t w[8];
+        words8(r.u[0], r.u[1], w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(w[i]);
+        if constexpr (XM == 2) {
+            uint32_t h[8];
+            words8(r.u[2], r.u[3], h);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) out[i] = __fadd_rn(out[i], __uint_as_float(h[i]));
+        }
     }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+template <int XM>
+__device__ __forceinline__ void load8(const void *__restrict__ x, int m, int K, int v, float out[8]) {
+    cvt8<XM>(load_raw8<XM>(x, m, K, v), out);
 }
 
-template <int MODE>
+__device__ __forceinline__ float max_abs8(const float f[8], float m) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    return m;
+}
+
+// q = clamp(rint(x * inv), -127, 127) for 8 values, packed little-endian.
+__device__ __forceinline__ uint2 quantize8(const float f[8], float inv) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float r = rintf(__fmul_rn(f[i], inv));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)r;
+        if (i < 4) lo |= b << (8 * i);
+        else hi |= b << (8 * (i - 4));
+    }
+    return make_uint2(lo, hi);
+}
+
+// Max over the 64 lanes of a wave with DPP row operations (max is idempotent,
+// so mirrored / broadcast partners may repeat): after the row steps every lane
+// of a 16-lane row holds the row max, the two broadcasts fold rows 0..3 into
+// lane 63, which is then read as a scalar.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+    v = fmaxf(v, dpp_f<0x142>(v));  // row_bcast:15
+    v = fmaxf(v, dpp_f<0x143>(v));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Workgroup barrier that waits only for this wave's LDS traffic: global loads
+// issued earlier stay in flight across it (a full __syncthreads() fence would
+// also drain them).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ==========================================================================
+// a4: per-token absmax int8 quantisation ([P2] "Architecture foundations":
+// 8-bit activations).  One 256-thread workgroup per token.  CPT > 0: each
+// thread keeps its CPT chunks of 8 values in registers (one read of the
+// token); CPT == 0: two passes over the token (any K).
+// amax is exact and independent of the reduction order; inv = 127/amax_c is
+// a correctly rounded division; the product x*inv is one fp32 multiply.
+// ==========================================================================
+template <int XM, int CPT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__ x, int K,
                                                          int8_t *__restrict__ q, float *__restrict__ s_a) {
     __shared__ float part[4];
     const int m = blockIdx.x;
     const int nvec = K >> 3;
+    constexpr int C = CPT > 0 ? CPT : 1;
+    float f[C][8];
     float amax = 0.0f;
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-        float f[8];
-        load8<MODE>(x, m, K, v, f);
+    if (CPT > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        for (int c = 0; c < C; ++c) {
+            const int v = threadIdx.x + 256 * c;
+            if (v < nvec) {
+                load8<XM>(x, m, K, v, f[c]);
+                amax = max_abs8(f[c], amax);
+            }
+        }
+    } else {
+        for (int v = threadIdx.x; v < nvec; v += 256) {
+            load8<XM>(x, m, K, v, f[0]);
+            amax = max_abs8(f[0], amax);
+        }
     }
     amax = wave_max(amax);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
@@ -115,48 +204,171 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
     const float amax_c = fmaxf(amax, 1e-5f);
     const float inv = __fdiv_rn(127.0f, amax_c);
     uint2 *qrow = reinterpret_cast<uint2 *>(q + (size_t)m * K);
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-        float f[8];
-        load8<MODE>(x, m, K, v, f);
-        uint32_t lo = 0, hi = 0;
+    if (CPT > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float r = rintf(__fmul_rn(f[i], inv));
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)r;
-            if (i < 4) lo |= b << (8 * i);
-            else hi |= b << (8 * (i - 4));
+        for (int c = 0; c < C; ++c) {
+            const int v = threadIdx.x + 256 * c;
+            if (v < nvec) qrow[v] = quantize8(f[c], inv);
         }
-        qrow[v] = make_uint2(lo, hi);
+    } else {
+        for (int v = threadIdx.x; v < nvec; v += 256) {
+            load8<XM>(x, m, K, v, f[0]);
+            qrow[v] = quantize8(f[0], inv);
+        }
     }
     if (threadIdx.x == 0) s_a[m] = __fdiv_rn(amax_c, 127.0f);
 }
 
 // ==========================================================================
-// a5: decode product, M <= 16.  One workgroup per 16-row tile, S waves split
-// the K blocks (split-K); wave w owns blocks [w*per, w*per + per).  Every lane
-// issues all of its weight, scale and activation loads for a chunk of NB
-// blocks before the first matrix-core step, so a wave keeps NB x 8 bytes per
-// lane of the weight stream in flight.  Partial sums are reduced through LDS
-// in wave order (deterministic).
-// MW = number of accumulator elements drained per lane (1, 2 or 4): with M <= 4
-// only tokens 0..M-1 (lanes 0..15, elements < M) are real.
+// a5: decode product, M <= 16.  One workgroup per 16-row tile; its nwc
+// compute waves split the K blocks (split-K), wave w owning blocks
+// [w*per, w*per + per).  Every lane issues all its weight and scale loads for
+// a chunk of NB blocks before the first matrix-core step (NB x 8 bytes per
+// lane of the weight stream in flight per wave).  Partial sums are reduced
+// through LDS in wave order, so results are deterministic.
+//
+// AM = -1: activations arrive quantised (int8 q, fp32 s_a).
+// AM = 0/1/2 (XM of load8): fused quantisation by QW extra "quant waves"
+// (waves nwc .. nwc+QW-1), token-parallel: quant wave qw handles tokens
+// qw, qw+QW, ...; it reads the token (pass 1: amax), re-reads it (pass 2:
+// quantise, same arithmetic as quant_act_kernel) and writes int8 into an LDS
+// copy of q.  The compute waves meanwhile have their weight loads in flight;
+// they wait at an LDS-only barrier (vmcnt is not drained), then read their
+// matrix-core operands from the LDS copy.  Every workgroup derives bit-
+// identical q and s_a, so the result equals quant-then-product.  Workgroup 0
+// optionally writes q and s_a out.
+// MW = accumulator elements drained per lane (1, 2 or 4): with M <= 4 only
+// tokens 0..M-1 (lanes 0..15, elements < M) carry data.
 // ==========================================================================
-template <int NB, int MW, bool INT_OUT>
-__global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ packed,
-                                                     const float *__restrict__ scales,
-                                                     const int8_t *__restrict__ q,
-                                                     const float *__restrict__ s_a,
-                                                     float *__restrict__ y, int32_t *__restrict__ acc_out,
-                                                     int M, int N, int K, int per) {
-    __shared__ int red[kMaxGemvWaves][4][kWave];
+struct GemvArgs {
+    const uint8_t *packed;
+    const float *scales;
+    const void *act;      // int8 q [M][K] (AM -1) or the unquantised activations
+    const float *s_a;     // AM -1 only
+    float *y;
+    int32_t *acc;
+    int8_t *q_out;        // optional (fused modes)
+    float *s_a_out;       // optional (fused modes)
+    int M, N, K, per, nwc, qw;
+};
+
+// LDS of the fused forms: [int8 copy of q, M*K bytes padded | reduction reuse]
+// then 16 fp32 dequant factors.
+__host__ __device__ inline size_t gemv_fused_region(int M, int K, int nwc) {
+    const size_t qbytes = ((size_t)M * K + 15) & ~(size_t)15;
+    const size_t red = (size_t)nwc * 4 * 64 * sizeof(int);
+    return qbytes > red ? qbytes : red;
+}
+
+template <int XM>
+__device__ void quant_wave(const GemvArgs &args, int8_t *qs, float *sa_lds, int qw, int l) {
+    const int M = args.M, K = args.K, nvec = K >> 3;
+    for (int m = qw; m < M; m += args.qw) {
+        float mx = 0.0f;
+        for (int c0 = 0; c0 < nvec; c0 += 4 * kWave) {
+            float f[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)  // unconditional (clamped) loads: all four in flight together
+                load8<XM>(args.act, m, K, min(c0 + u * kWave + l, nvec - 1), f[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mx = max_abs8(f[u], mx);  // a clamped repeat cannot change the max
+        }
+        const float amax_c = fmaxf(wave_max(mx), 1e-5f);
+        const float inv = __fdiv_rn(127.0f, amax_c);
+        for (int c0 = 0; c0 < nvec; c0 += 4 * kWave) {
+            float f[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load8<XM>(args.act, m, K, min(c0 + u * kWave + l, nvec - 1), f[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * kWave + l;
+                if (c < nvec) {
+                    const uint2 qv = quantize8(f[u], inv);
+                    *reinterpret_cast<uint2 *>(qs + (size_t)m * K + 8 * c) = qv;
+                    if (args.q_out && blockIdx.x == 0)
+                        *reinterpret_cast<uint2 *>(args.q_out + (size_t)m * K + 8 * c) = qv;
+                }
+            }
+        }
+        const float sa = __fdiv_rn(amax_c, 127.0f);
+        if (l == 0) {
+            sa_lds[m] = sa;
+            if (args.s_a_out && blockIdx.x == 0) args.s_a_out[m] = sa;
+        }
+    }
+}
+
+// Kernel forms.
+enum GemvForm {
+    kDirect = 0,    // int8 q from global memory, one chunk of blocks per wave
+    kMulti = 1,     // as kDirect with a loop over chunks (K beyond 12 x 8 blocks)
+    kStaged = 2,    // int8 q slice fetched with a few coalesced loads into LDS (M <= 4)
+    kAllWaves = 3,  // fused quantisation, every compute wave quantises its own K-slice (M <= 4)
+    kQuantWaves = 4 // fused quantisation by 4 extra quant waves (4 < M <= 16)
+};
+
+template <int AM, int NB, int MW, bool INT_OUT, int FORM>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int M = args.M, N = args.N, K = args.K, per = args.per, nwc = args.nwc;
     const int nblk = K >> 7;
     const int tile = blockIdx.x;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
-    const int nw = blockDim.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
+    const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+    constexpr int NE = INT_OUT ? 4 : MW;
+    constexpr bool FUSED = AM >= 0;
+    constexpr bool LDSQ = FORM == kStaged || FORM == kAllWaves || FORM == kQuantWaves;  // operands via LDS
+    constexpr int XM = AM < 0 ? 0 : AM;
+    int *red = reinterpret_cast<int *>(smem);
+    int8_t *qs = reinterpret_cast<int8_t *>(smem);
+    // LDS forms: after the q region, 16 dequant factors then [12 waves][4 tokens] partial amax
+    float *tail = reinterpret_cast<float *>(smem + (LDSQ ? gemv_fused_region(M, K, nwc) : 0));
+
+    if (FORM == kQuantWaves && w >= nwc) {
+        quant_wave<XM>(args, qs, tail, w - nwc, l);
+        lds_barrier();  // q ready
+        lds_barrier();  // operands consumed
+        lds_barrier();  // partial sums written
+        return;
+    }
+
     const int bw0 = w * per;
     const int bw1 = min(nblk, bw0 + per);
+    const int nbw = bw1 - bw0;
     const bool tok = j < M;
+
+    // vmcnt retires loads in issue order: whatever is needed before the
+    // weights arrive (activations to quantise or stage) is issued before them.
+    float sa_pre[NE];
+    if (!FUSED && !INT_OUT) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) sa_pre[e] = args.s_a[min(4 * g + e, M - 1)];
+    }
+    // kAllWaves: this wave's K-slice of every token, raw, 8 values per chunk
+    constexpr int CR = (NB + 3) / 4;
+    Raw8<XM> xr[FORM == kAllWaves ? MW : 1][FORM == kAllWaves ? CR : 1];
+    const int nchw = nbw * 16;
+    if (FORM == kAllWaves) {
+#pragma unroll
+        for (int m = 0; m < (FORM == kAllWaves ? MW : 1); ++m)
+#pragma unroll
+            for (int r = 0; r < (FORM == kAllWaves ? CR : 1); ++r)
+                xr[m][r] = load_raw8<XM>(args.act, min(m, M - 1), K, bw0 * 16 + min(l + kWave * r, nchw - 1));
+    }
+    // kStaged: this wave's K-slice of q for M <= MW tokens in 16-byte chunks
+    constexpr int QR = (MW * NB + 7) / 8;
+    uint4 qraw[FORM == kStaged ? QR : 1];
+    const int qper = nbw * 8;  // chunks per token
+    if (FORM == kStaged) {
+        const int8_t *q = static_cast<const int8_t *>(args.act);
+#pragma unroll
+        for (int r = 0; r < (FORM == kStaged ? QR : 1); ++r) {
+            const int c = min(l + kWave * r, M * qper - 1);
+            const int m = c / qper, o = c - m * qper;
+            qraw[r] = *reinterpret_cast<const uint4 *>(q + (size_t)m * K + (size_t)bw0 * kBlockK + 16 * o);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     float yacc[MW];
     int iacc[4];
@@ -165,29 +377,91 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 #pragma unroll
     for (int e = 0; e < 4; ++e) iacc[e] = 0;
 
-    for (int c0 = bw0; c0 < bw1; c0 += NB) {
+    const int8_t *qsrc = LDSQ ? qs : static_cast<const int8_t *>(args.act);
+
+    // One chunk of up to NB blocks: all its loads, then its matrix-core steps.
+    auto chunk = [&](const int c0) {
         const int nb = min(NB, bw1 - c0);
-        const uint8_t *wp = packed + ((size_t)tile * nblk + c0) * kBrickBytes + l * 8;
-        const float *sp = scales + ((size_t)tile * nblk + c0) * kTileN + j;
-        const int8_t *qp = q + (size_t)j * K + (size_t)c0 * kBlockK + g * 16;
+        const uint8_t *wp = args.packed + ((size_t)tile * nblk + c0) * kBrickBytes + l * 8;
+        const float *sp = args.scales + ((size_t)tile * nblk + c0) * kTileN + j;
         uint2 wv[NB];
         float sc[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {  // unconditional (clamped) loads, issued back to back
+            const int bi = min(i, nb - 1);
+            wv[i] = *reinterpret_cast<const uint2 *>(wp + bi * kBrickBytes);
+            if (!INT_OUT) sc[i] = sp[bi * kTileN];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FORM == kStaged) {
+#pragma unroll
+            for (int r = 0; r < QR; ++r) {
+                const int c = l + kWave * r;
+                if (c < M * qper) {
+                    const int m = c / qper, o = c - m * qper;
+                    *reinterpret_cast<uint4 *>(qs + (size_t)m * K + (size_t)bw0 * kBlockK + 16 * o) = qraw[r];
+                }
+            }
+            // the wave reads back only its own slice: LDS keeps one wave's accesses in order
+        } else if constexpr (FORM == kAllWaves) {
+            float *amax_part = tail + 16;
+            float xf[MW][CR][8];
+#pragma unroll
+            for (int m = 0; m < MW; ++m)
+#pragma unroll
+                for (int r = 0; r < CR; ++r) cvt8<XM>(xr[m][r], xf[m][r]);
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int r = 0; r < CR; ++r)
+                    if (l + kWave * r < nchw) mx = max_abs8(xf[m][r], mx);
+                mx = wave_max(mx);
+                if (l == 0) amax_part[w * 4 + m] = mx;
+            }
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                if (m >= M) break;
+                float am = 0.0f;
+                for (int ww = 0; ww < nwc; ++ww) am = fmaxf(am, amax_part[ww * 4 + m]);
+                const float amax_c = fmaxf(am, 1e-5f);
+                const float inv = __fdiv_rn(127.0f, amax_c);
+#pragma unroll
+                for (int r = 0; r < CR; ++r) {
+                    const int c = l + kWave * r;
+                    if (c < nchw) {
+                        const uint2 qv = quantize8(xf[m][r], inv);
+                        const size_t off = (size_t)m * K + (size_t)bw0 * kBlockK + 8 * c;
+                        *reinterpret_cast<uint2 *>(qs + off) = qv;
+                        if (args.q_out && blockIdx.x == 0) *reinterpret_cast<uint2 *>(args.q_out + off) = qv;
+                    }
+                }
+                if (w == 0 && l == 0) {
+                    const float sa = __fdiv_rn(amax_c, 127.0f);
+                    tail[m] = sa;
+                    if (args.s_a_out && blockIdx.x == 0) args.s_a_out[m] = sa;
+                }
+            }
+            // no barrier: each wave reads back only the slice it wrote itself
+        } else if constexpr (FORM == kQuantWaves) {
+            lds_barrier();  // q ready (written by the quant waves)
+        }
+        const int8_t *qp = qsrc + (size_t)j * K + (size_t)c0 * kBlockK + g * 16;
         v4i a[NB][2];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            if (i < nb) {
-                wv[i] = *reinterpret_cast<const uint2 *>(wp + i * kBrickBytes);
-                if (!INT_OUT) sc[i] = sp[i * kTileN];
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) a[i][s] = v4i{0, 0, 0, 0};
+        if (tok) {  // only lanes of real tokens fetch operands (padding lanes stay zero)
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int bi = min(i, nb - 1);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) a[i][s] = *reinterpret_cast<const v4i *>(qp + bi * kBlockK + s * 64);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                a[i][s] = v4i{0, 0, 0, 0};
-                if (i < nb && tok) a[i][s] = *reinterpret_cast<const v4i *>(qp + i * kBlockK + s * 64);
-            }
-        }
+        __builtin_amdgcn_sched_barrier(0);  // keep every load above the first matrix-core step
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i < nb) {
@@ -203,12 +477,20 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
                 }
             }
         }
+    };
+    // Straight-line for a single chunk; the chunk loop is a separate form,
+    // because a loop makes the wait-count pass drain the early loads at its header.
+    if constexpr (FORM == kMulti) {
+        for (int c0 = bw0; c0 < bw1; c0 += NB) chunk(c0);
+    } else {
+        chunk(bw0);
     }
 
-    constexpr int NE = INT_OUT ? 4 : MW;
+    if (LDSQ) lds_barrier();  // the reduction buffer overlaps the LDS copy of q
 #pragma unroll
-    for (int e = 0; e < NE; ++e) red[w][e][l] = INT_OUT ? iacc[e] : __float_as_int(yacc[e]);
-    __syncthreads();
+    for (int e = 0; e < NE; ++e) red[(w * 4 + e) * kWave + l] = INT_OUT ? iacc[e] : __float_as_int(yacc[e]);
+    if (LDSQ) lds_barrier();
+    else __syncthreads();
     if (w == 0) {
         const int n = tile * kTileN + j;
 #pragma unroll
@@ -216,12 +498,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
             const int m = 4 * g + e;
             if (INT_OUT) {
                 int sum = 0;
-                for (int ww = 0; ww < nw; ++ww) sum += red[ww][e][l];
-                if (m < M) acc_out[(size_t)m * N + n] = sum >> 6;  // exact: sum is 64 * integer
+                for (int ww = 0; ww < nwc; ++ww) sum += red[(ww * 4 + e) * kWave + l];
+                if (m < M) args.acc[(size_t)m * N + n] = sum >> 6;  // exact: sum is 64 * integer
             } else {
                 float sum = 0.0f;
-                for (int ww = 0; ww < nw; ++ww) sum += __int_as_float(red[ww][e][l]);
-                if (m < M) y[(size_t)m * N + n] = sum * (s_a[m] * 0.015625f);
+                for (int ww = 0; ww < nwc; ++ww) sum += __int_as_float(red[(ww * 4 + e) * kWave + l]);
+                if (m < M) {
+                    const float sa = FUSED ? tail[m] : sa_pre[e];
+                    args.y[(size_t)m * N + n] = sum * (sa * 0.015625f);
+                }
             }
         }
     }
@@ -363,40 +648,107 @@ bitnet_status_t launched() {
     return hipGetLastError() == hipSuccess ? BITNET_OK : BITNET_ERR_HIP;
 }
 
-template <int NB, bool INT_OUT>
-void gemv_launch_mw(int mw, dim3 grid, dim3 block, hipStream_t st, const uint8_t *p, const float *s,
-                    const int8_t *q, const float *sa, float *y, int32_t *acc, int M, int N, int K, int per) {
-    if (INT_OUT || mw == 4)
-        hipLaunchKernelGGL((gemv_kernel<NB, 4, INT_OUT>), grid, block, 0, st, p, s, q, sa, y, acc, M, N, K, per);
+template <int AM, int NB, bool INT_OUT, int FORM>
+void gemv_launch_mw(int mw, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
+    if (FORM == kQuantWaves || INT_OUT || mw == 4)
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, INT_OUT, FORM>), grid, block, lds, st, a);
     else if (mw == 2)
-        hipLaunchKernelGGL((gemv_kernel<NB, 2, INT_OUT>), grid, block, 0, st, p, s, q, sa, y, acc, M, N, K, per);
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, INT_OUT, FORM>), grid, block, lds, st, a);
     else
-        hipLaunchKernelGGL((gemv_kernel<NB, 1, INT_OUT>), grid, block, 0, st, p, s, q, sa, y, acc, M, N, K, per);
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, INT_OUT, FORM>), grid, block, lds, st, a);
 }
 
-template <bool INT_OUT>
-void gemv_launch(const uint8_t *p, const float *s, const int8_t *q, const float *sa, float *y, int32_t *acc,
-                 int M, int N, int K, hipStream_t st) {
+template <int AM, int NB, bool INT_OUT>
+void gemv_launch_form(int form, int mw, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
+    if constexpr (AM >= 0) {
+        if (form == kQuantWaves) gemv_launch_mw<AM, NB, false, kQuantWaves>(mw, grid, block, lds, st, a);
+        else gemv_launch_mw<AM, NB, false, kAllWaves>(mw, grid, block, lds, st, a);
+    } else {
+        if (form == kStaged) gemv_launch_mw<AM, NB, INT_OUT, kStaged>(mw, grid, block, lds, st, a);
+        else if (NB == 8 && form == kMulti) gemv_launch_mw<AM, 8, INT_OUT, kMulti>(mw, grid, block, lds, st, a);
+        else gemv_launch_mw<AM, NB, INT_OUT, kDirect>(mw, grid, block, lds, st, a);
+    }
+}
+
+constexpr size_t kMaxLds = 65536;
+
+#ifndef BITNET_GEMV_BLOCKS_PER_WAVE
+#define BITNET_GEMV_BLOCKS_PER_WAVE 4
+#endif
+#ifndef BITNET_GEMV_MAX_WAVES
+#define BITNET_GEMV_MAX_WAVES 12
+#endif
+// Split-K geometry of the decode product: about 4 blocks per wave, at most 12
+// compute waves per workgroup (room for up to 4 quant waves in the fused
+// form), no idle wave.  Every form uses the same geometry and the same
+// summation order, so their fp32 results are bit-identical.
+constexpr int kMaxSplitWaves = BITNET_GEMV_MAX_WAVES;
+constexpr int kBlocksPerWave = BITNET_GEMV_BLOCKS_PER_WAVE;
+void gemv_split(int K, int *nw_out, int *per_out) {
     const int nblk = K / (int)kBlockK;
-    // split-K: about 4 blocks per wave, at most 16 waves per workgroup
-    int nw = (nblk + 3) / 4;
-    if (nw > kMaxGemvWaves) nw = kMaxGemvWaves;
+    int nw = (nblk + kBlocksPerWave - 1) / kBlocksPerWave;
+    if (nw > kMaxSplitWaves) nw = kMaxSplitWaves;
     if (nw < 1) nw = 1;
     const int per = (nblk + nw - 1) / nw;
-    nw = (nblk + per - 1) / per;  // no idle wave
-    const int nb = per < 8 ? per : 8;
-    const int mw = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    dim3 grid(N / (int)kTileN), block(kWave * nw);
-    switch (nb) {
-        case 1: gemv_launch_mw<1, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 2: gemv_launch_mw<2, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 3: gemv_launch_mw<3, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 4: gemv_launch_mw<4, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 5: gemv_launch_mw<5, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 6: gemv_launch_mw<6, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        case 7: gemv_launch_mw<7, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
-        default: gemv_launch_mw<8, INT_OUT>(mw, grid, block, st, p, s, q, sa, y, acc, M, N, K, per); break;
+    *nw_out = (nblk + per - 1) / per;
+    *per_out = per;
+}
+
+size_t gemv_fused_lds(int M, int K, int nw) { return gemv_fused_region(M, K, nw) + (16 + 48) * sizeof(float); }
+
+// Picks the form and launches.  Returns false (nothing launched) if a fused
+// form was asked for and does not fit.
+template <int AM, bool INT_OUT>
+bool gemv_launch(GemvArgs a, hipStream_t st) {
+    int nw, per;
+    gemv_split(a.K, &nw, &per);
+    a.per = per;
+    a.nwc = nw;
+    int form;
+    size_t lds;
+    if (AM >= 0) {
+        if (per > 8) return false;
+        form = a.M <= 4 ? kAllWaves : kQuantWaves;
+        a.qw = form == kQuantWaves ? 4 : 0;
+        lds = gemv_fused_lds(a.M, a.K, nw);
+        if (lds > kMaxLds) return false;
+    } else {
+        a.qw = 0;
+        if (per > 8) {
+            form = kMulti;
+            lds = (size_t)nw * 4 * kWave * sizeof(int);
+        } else if (a.M <= 4 && gemv_fused_lds(a.M, a.K, nw) <= kMaxLds) {
+            form = kStaged;
+            lds = gemv_fused_lds(a.M, a.K, nw);
+        } else {
+            form = kDirect;
+            lds = (size_t)nw * 4 * kWave * sizeof(int);
+        }
     }
+    const int nb = per < 8 ? per : 8;
+    const int mw = a.M == 1 ? 1 : (a.M == 2 ? 2 : 4);
+    dim3 grid(a.N / (int)kTileN), block(kWave * (nw + a.qw));
+    switch (nb) {
+        case 1: gemv_launch_form<AM, 1, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 2: gemv_launch_form<AM, 2, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 3: gemv_launch_form<AM, 3, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 4: gemv_launch_form<AM, 4, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 5: gemv_launch_form<AM, 5, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 6: gemv_launch_form<AM, 6, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 7: gemv_launch_form<AM, 7, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        default: gemv_launch_form<AM, 8, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+    }
+    return true;
+}
+
+template <int XM>
+void quant_launch(const void *x, int M, int K, int8_t *q, float *s_a, hipStream_t st) {
+    const int nvec = K / 8;
+    if (nvec <= 256) hipLaunchKernelGGL((quant_act_kernel<XM, 1>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
+    else if (nvec <= 512) hipLaunchKernelGGL((quant_act_kernel<XM, 2>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
+    else if (nvec <= 1024) hipLaunchKernelGGL((quant_act_kernel<XM, 4>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
+    else if (nvec <= 2048) hipLaunchKernelGGL((quant_act_kernel<XM, 8>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
+    else hipLaunchKernelGGL((quant_act_kernel<XM, 0>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
 }
 
 template <int OUT>
@@ -427,17 +779,15 @@ bitnet_status_t bitnet_quant_act(const void *x, int xdt, int M, int K, int8_t *q
     if (!x || !q || !s_a || !aligned(x, 16) || !aligned(q, 16) || !aligned(s_a, 4)) return BITNET_ERR_INVALID_ARG;
     if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
     if (M < 1 || M > 65535 * 1024 || K < 16 || K % 16) return BITNET_ERR_UNSUPPORTED_SHAPE;
-    if (xdt == BITNET_DT_BF16)
-        hipLaunchKernelGGL(quant_act_kernel<0>, dim3(M), dim3(256), 0, stream, x, K, q, s_a);
-    else
-        hipLaunchKernelGGL(quant_act_kernel<1>, dim3(M), dim3(256), 0, stream, x, K, q, s_a);
+    if (xdt == BITNET_DT_BF16) quant_launch<0>(x, M, K, q, s_a, stream);
+    else quant_launch<1>(x, M, K, q, s_a, stream);
     return launched();
 }
 
 bitnet_status_t bitnet_quant_act_fold(const float *y, int M, int H, int8_t *q, float *s_a, hipStream_t stream) {
     if (!y || !q || !s_a || !aligned(y, 16) || !aligned(q, 16) || !aligned(s_a, 4)) return BITNET_ERR_INVALID_ARG;
     if (M < 1 || M > 65535 * 1024 || H < 16 || H % 16) return BITNET_ERR_UNSUPPORTED_SHAPE;
-    hipLaunchKernelGGL(quant_act_kernel<2>, dim3(M), dim3(256), 0, stream, (const void *)y, H, q, s_a);
+    quant_launch<2>(y, M, H, q, s_a, stream);
     return launched();
 }
 
@@ -447,7 +797,8 @@ bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, con
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 4))
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
-    gemv_launch<false>(packed, scales, q, s_a, y, nullptr, M, N, K, stream);
+    GemvArgs a{packed, scales, q, s_a, y, nullptr, nullptr, nullptr, M, N, K, 0, 0, 0};
+    gemv_launch<-1, false>(a, stream);
     return launched();
 }
 
@@ -463,12 +814,36 @@ bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, con
     return launched();
 }
 
+bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales, const void *x, int xdt,
+                                     float *y, int8_t *q_out, float *s_a_out, int M, int N, int K,
+                                     hipStream_t stream) {
+    if (!packed || !scales || !x || !y) return BITNET_ERR_INVALID_ARG;
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(x, 16) || !aligned(y, 4) ||
+        !aligned(q_out, 16) || !aligned(s_a_out, 4))
+        return BITNET_ERR_INVALID_ARG;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32 && xdt != BITNET_DT_F32_FOLD2) return BITNET_ERR_INVALID_ARG;
+    if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    int nw, per;
+    gemv_split(K, &nw, &per);
+    if (per > 8 || gemv_fused_lds(M, K, nw) > kMaxLds) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    GemvArgs a{packed, scales, x, nullptr, y, nullptr, q_out, s_a_out, M, N, K, 0, 0, 0};
+    bool ok;
+    if (xdt == BITNET_DT_BF16) ok = gemv_launch<0, false>(a, stream);
+    else if (xdt == BITNET_DT_F32) ok = gemv_launch<1, false>(a, stream);
+    else ok = gemv_launch<2, false>(a, stream);
+    if (!ok) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    return launched();
+}
+
 bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int32_t *acc, int M, int N, int K,
                                     hipStream_t stream) {
     if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 4))
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
-    if (M <= kGemvMaxM) gemv_launch<true>(packed, nullptr, q, nullptr, nullptr, acc, M, N, K, stream);
+    if (M <= kGemvMaxM) {
+        GemvArgs a{packed, nullptr, q, nullptr, nullptr, acc, nullptr, nullptr, M, N, K, 0, 0, 0};
+        gemv_launch<-1, true>(a, stream);
+    }
     else gemm_launch<2>(packed, nullptr, q, nullptr, acc, M, N, K, stream);
     return launched();
 }

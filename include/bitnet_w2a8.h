@@ -71,7 +71,11 @@ typedef enum {
     BITNET_ERR_HIP = 3                /* a HIP launch or runtime call failed */
 } bitnet_status_t;
 
-typedef enum { BITNET_DT_BF16 = 0, BITNET_DT_F32 = 1 } bitnet_dtype_t;
+typedef enum {
+    BITNET_DT_BF16 = 0,      /* bfloat16 */
+    BITNET_DT_F32 = 1,       /* fp32 */
+    BITNET_DT_F32_FOLD2 = 2  /* fp32 [M][2K] read as h = x[:, :K] + x[:, K:] (one fp32 add) */
+} bitnet_dtype_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitnet_status_str(int status);
@@ -152,6 +156,24 @@ bitnet_status_t bitnet_quant_act_fold(const float *y, int M, int H, int8_t *q, f
  * max(|y|, s_a * sum_b |S*A|). */
 bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q,
                                  const float *s_a, float *y, int M, int N, int K, hipStream_t stream);
+
+/* Decode step in one launch: quantise the activations exactly as
+ * bitnet_quant_act does (per-token absmax, fp32, half to even) and multiply, as
+ * bitnet_w2a8_gemv does.  Each workgroup derives the same int8 values and
+ * factors, so y equals bitnet_quant_act followed by bitnet_w2a8_gemv.
+ *   x        device, xdt BITNET_DT_BF16 or BITNET_DT_F32: [M][K];
+ *            BITNET_DT_F32_FOLD2: fp32 [M][2K], quantised input h = x[:, :K] + x[:, K:]
+ *            (the junction of a stacked decode chain, as bitnet_quant_act_fold)
+ *   y        device, fp32 [M][N] (out)
+ *   q_out    device, int8 [M][K] (out, optional: NULL to skip)
+ *   s_a_out  device, fp32 [M] (out, optional: NULL to skip)
+ *   packed, scales as bitnet_w2a8_gemv.
+ * Rules: 1 <= M <= 16, the shape rules, K <= 12288 and M*K <= 64512 (the int8
+ * copy of the activations lives in LDS); otherwise BITNET_ERR_UNSUPPORTED_SHAPE
+ * and the caller uses bitnet_quant_act + bitnet_w2a8_gemv. */
+bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales, const void *x, int xdt,
+                                     float *y, int8_t *q_out, float *s_a_out, int M, int N, int K,
+                                     hipStream_t stream);
 
 /* Prefill product for any M >= 1 on the int8 matrix cores; y is [M][N] in
  * dtype ydt (BITNET_DT_BF16: fp32 value rounded to nearest even; or

@@ -173,6 +173,48 @@ def test_zero_weights_and_zero_tokens(gpu):
     assert np.all(host(bn.bitnet_w2a8_gemm(pz, sz, q, s, N, K, out_dtype=torch.float32)) == 0.0)
 
 
+# ------------------------------------------------------------------ fused quantise-and-multiply
+@pytest.mark.parametrize("mode", ["bf16", "f32", "fold"])
+@pytest.mark.parametrize("M,N,K", [(1, 48, 384), (2, 272, 2688), (3, 80, 640), (5, 160, 6912), (8, 2064, 2560),
+                                   (16, 32, 128), (1, 64, 12288)])
+def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
+    c = wl.small_case(M * 5 + N + K, M, N, K, xkind="t3")
+    p, st = pack_dev(c.T, c.S)
+    if mode == "bf16":
+        xd = x_dev(c.x_bits)
+        qo, so = oracle.quant_act_bf16(c.x_bits)
+        qd, sd = bn.bitnet_quant_act(xd)
+    else:
+        x = wl.bf16_to_f32(c.x_bits) * np.float32(0.37)
+        if mode == "fold":
+            x = np.concatenate([x, wl.rng_for(61, M, K).standard_normal((M, K)).astype(np.float32)], axis=1)
+            qo, so = oracle.fold_quant(x)
+            xd = dev(x)
+            qd, sd = bn.bitnet_quant_act_fold(xd)
+        else:
+            qo, so = oracle.quant_act_f32(x)
+            xd = dev(x)
+            qd, sd = bn.bitnet_quant_act(xd)
+    q_out = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_out = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = bn.bitnet_w2a8_gemv_act(p, st, xd, N, K, fold=(mode == "fold"), q_out=q_out, s_a_out=s_out)
+    y_ref = bn.bitnet_w2a8_gemv(p, st, qd, sd, N, K)
+    assert np.array_equal(host(q_out), qo) and np.array_equal(host(s_out), so)
+    yh = host(y)
+    assert np.array_equal(yh.view(np.uint32), host(y_ref).view(np.uint32)), "fused and unfused differ"
+    assert_f32_close(yh, oracle_ref(c.T, c.S, qo, so), f"gemv_act {mode} {M}x{N}x{K}")
+
+
+def test_gemv_act_rejects_what_does_not_fit(gpu):
+    # M*K beyond the LDS copy of q, and K beyond 12 waves x 8 blocks
+    for (M, K) in [(16, 8192), (1, 12288 + 128)]:
+        p, st = pack_dev(np.zeros((16, K), np.int8), np.ones((16, K // 128), np.float32))
+        x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(bn.BitnetError) as ei:
+            bn.bitnet_w2a8_gemv_act(p, st, x, 16, K)
+        assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+
+
 # ------------------------------------------------------------------ full-size workloads
 def _full_gemv(c, T, S, what):
     # end to end on the device: bf16 activations -> quant -> product
