@@ -199,6 +199,34 @@ def prefill_shape(torch, bn, wl, reps=10):
     }
 
 
+def stack_shape(torch, bn, wl, Ms=(1, 8), reps=20):
+    """The 30-layer decode stack (4 x 2560x2560, 13824x2560, 2560x6912 per layer):
+    one token = one bitnet_w2a8_chain call (180 products), captured as a graph."""
+    t0 = time.perf_counter()
+    ws, folds, pbytes = [], [], 0
+    for layer in range(wl.STACK_LAYERS):
+        for idx in range(6):
+            T, S = wl.stack_matrix(layer, idx)
+            ws.append(bn.PackedWeight.from_ternary(T, S))
+            folds.append(idx == 5)
+            pbytes += T.size // 4
+    chain = bn.Chain(ws, folds)
+    setup_s = time.perf_counter() - t0
+    out = []
+    for M in Ms:
+        x = torch.from_numpy(wl.stack_input(M).view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, wl.STACK_HIDDEN), dtype=torch.float32, device="cuda")
+        chain.workspace(M)
+        us = graph_us_per_launch(torch, lambda i: chain(x, y=y), 1, reps)
+        out.append({"shape": "stack_30x6_decode", "M": M, "token_step_us": us, "tokens_per_s": M * 1e6 / us,
+                    "products_per_token": len(ws), "packed_bytes_per_token": pbytes,
+                    "packed_GBps": pbytes / us / 1e3, "pct_hbm_packed": 100.0 * pbytes / us / 1e3 / HBM_PEAK_GBS,
+                    "setup_s": setup_s})
+    del chain, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------
 def cpu_baseline(wl, c, T, S, seconds):
     """The oracle, as it stands, timed single-threaded on this host on the
@@ -334,6 +362,9 @@ def main():
         r = prefill_shape(torch, bn, wl)
         log(json.dumps(r))
         shapes.append(r)
+        for r in stack_shape(torch, bn, wl):
+            log(json.dumps(r))
+            shapes.append(r)
         result["shapes"] = shapes
 
     if not args.no_cpu:

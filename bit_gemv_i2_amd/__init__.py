@@ -55,7 +55,16 @@ _SIGS = {
     "bitnet_w2a8_gemv_act": ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3
                              + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_acc_i32": ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_chain_workspace_bytes": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+    "bitnet_w2a8_chain": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
 }
+
+
+class ChainLayer(ctypes.Structure):
+    """bitnet_chain_layer_t"""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int),
+                ("fold_input", ctypes.c_int)]
 
 
 def lib():
@@ -296,3 +305,45 @@ class PackedWeight:
     def gemm(self, q, s_a, out_dtype=None, y=None, stream=None):
         return bitnet_w2a8_gemm(self.packed, self.scales, q, s_a, self.N, self.K, out_dtype=out_dtype, y=y,
                                 stream=stream)
+
+
+# ------------------------------------------------------------------ chained decode
+class Chain:
+    """A stack of W2A8 layers run by bitnet_w2a8_chain.  `weights` are
+    PackedWeight objects; `folds[i]` marks a layer whose input is the previous
+    output folded in half (h = lo + hi)."""
+
+    def __init__(self, weights, folds=None):
+        self.weights = list(weights)
+        self.folds = [False] * len(self.weights) if folds is None else [bool(f) for f in folds]
+        n = len(self.weights)
+        self._arr = (ChainLayer * n)()
+        for i, (w, f) in enumerate(zip(self.weights, self.folds)):
+            self._arr[i] = ChainLayer(w.packed.data_ptr(), w.scales.data_ptr(), w.N, w.K, int(f))
+        self._ws = {}
+
+    def workspace_bytes(self, M: int) -> int:
+        return lib().bitnet_w2a8_chain_workspace_bytes(ctypes.cast(self._arr, ctypes.c_void_p), len(self.weights), M)
+
+    def workspace(self, M: int, device="cuda"):
+        import torch
+        if M not in self._ws:
+            nb = self.workspace_bytes(M)
+            if nb == 0:
+                raise BitnetError(BITNET_ERR_UNSUPPORTED_SHAPE, "bitnet_w2a8_chain_workspace_bytes")
+            self._ws[M] = torch.empty(nb, dtype=torch.uint8, device=device)
+        return self._ws[M]
+
+    def __call__(self, x, y=None, stream=None):
+        import torch
+        M = x.shape[0]
+        xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
+        if xdt is None:
+            raise ValueError("x must be bf16 or fp32")
+        if y is None:
+            y = torch.empty((M, self.weights[-1].N), dtype=torch.float32, device=x.device)
+        ws = self.workspace(M, x.device)
+        _ok(lib().bitnet_w2a8_chain(ctypes.cast(self._arr, ctypes.c_void_p), len(self.weights), _dev_ptr(x, "x"), xdt,
+                                    M, _dev_ptr(y, "y"), _dev_ptr(ws, "workspace"), ws.numel(), _stream(stream)),
+            "bitnet_w2a8_chain")
+        return y

@@ -839,13 +839,105 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
                                     hipStream_t stream) {
     if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 4))
         return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    // the int32 accumulators hold 64 * sum: |64 * 127 * K| < 2^31
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M) || K > 262144) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (M <= kGemvMaxM) {
         GemvArgs a{packed, nullptr, q, nullptr, nullptr, acc, nullptr, nullptr, M, N, K, 0, 0, 0};
         gemv_launch<-1, true>(a, stream);
     }
     else gemm_launch<2>(packed, nullptr, q, nullptr, acc, M, N, K, stream);
     return launched();
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// a7: a chain of products with per-token requantisation between them (the
+// decode pass through a stack of BitNet linear layers).  Host-side loop that
+// enqueues one fused quantise-and-multiply launch per layer (M <= 4), or a
+// quantisation launch and a product launch; intermediate fp32 activations
+// ping-pong between two halves of the caller's workspace.
+// --------------------------------------------------------------------------
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct ChainPlan {
+    size_t act_bytes;  // one fp32 activation buffer: M * max N
+    size_t q_bytes;    // int8 q: M * max K
+    size_t total;
+};
+
+bitnet_status_t chain_plan(const bitnet_chain_layer_t *layers, int n, int M, int x_width, ChainPlan *plan) {
+    if (!layers || n < 1 || M < 1 || M > kGemvMaxM) return BITNET_ERR_INVALID_ARG;
+    int64_t maxN = 0, maxK = 0;
+    for (int i = 0; i < n; ++i) {
+        const bitnet_chain_layer_t &L = layers[i];
+        if (!L.packed || !L.scales || !aligned(L.packed, 16) || !aligned(L.scales, 16)) return BITNET_ERR_INVALID_ARG;
+        if (!shape_ok(L.N, L.K)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        const int in = i == 0 ? x_width : layers[i - 1].N;
+        if (L.fold_input ? (in != 2 * L.K) : (in != L.K)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        if (i == 0 && L.fold_input) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        maxN = L.N > maxN ? L.N : maxN;
+        maxK = L.K > maxK ? L.K : maxK;
+    }
+    plan->act_bytes = align256((size_t)M * maxN * sizeof(float));
+    plan->q_bytes = align256((size_t)M * maxK);
+    plan->total = 2 * plan->act_bytes + plan->q_bytes + 256;
+    return BITNET_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int n, int M) {
+    ChainPlan plan;
+    if (!layers || n < 1) return 0;
+    return chain_plan(layers, n, M, layers[0].K, &plan) == BITNET_OK ? plan.total : 0;
+}
+
+bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
+                                  float *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!x || !y || !workspace || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 256))
+        return BITNET_ERR_INVALID_ARG;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
+    if (!layers || n < 1) return BITNET_ERR_INVALID_ARG;
+    ChainPlan plan;
+    const bitnet_status_t st = chain_plan(layers, n, M, layers[0].K, &plan);
+    if (st != BITNET_OK) return st;
+    if (workspace_bytes < plan.total) return BITNET_ERR_INVALID_ARG;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *act[2] = {reinterpret_cast<float *>(ws), reinterpret_cast<float *>(ws + plan.act_bytes)};
+    int8_t *q = reinterpret_cast<int8_t *>(ws + 2 * plan.act_bytes);
+    float *s_a = reinterpret_cast<float *>(ws + 2 * plan.act_bytes + plan.q_bytes);
+
+    const void *in = x;
+    int in_dt = xdt;
+    for (int i = 0; i < n; ++i) {
+        const bitnet_chain_layer_t &L = layers[i];
+        float *out = (i == n - 1) ? y : act[i & 1];
+        const int dt = L.fold_input ? BITNET_DT_F32_FOLD2 : in_dt;
+        int nw, per;
+        gemv_split(L.K, &nw, &per);
+        const bool fused = M <= 4 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds;
+        if (fused) {
+            GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
+            bool ok;
+            if (dt == BITNET_DT_BF16) ok = gemv_launch<0, false>(a, stream);
+            else if (dt == BITNET_DT_F32) ok = gemv_launch<1, false>(a, stream);
+            else ok = gemv_launch<2, false>(a, stream);
+            if (!ok) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        } else {
+            if (dt == BITNET_DT_BF16) quant_launch<0>(in, M, L.K, q, s_a, stream);
+            else if (dt == BITNET_DT_F32) quant_launch<1>(in, M, L.K, q, s_a, stream);
+            else quant_launch<2>(in, M, L.K, q, s_a, stream);
+            GemvArgs a{L.packed, L.scales, q, s_a, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
+            gemv_launch<-1, false>(a, stream);
+        }
+        if (hipGetLastError() != hipSuccess) return BITNET_ERR_HIP;
+        in = out;
+        in_dt = BITNET_DT_F32;
+    }
+    return BITNET_OK;
 }
 
 }  // extern "C"

@@ -182,6 +182,38 @@ bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, con
                                  const float *s_a, void *y, int ydt, int M, int N, int K,
                                  hipStream_t stream);
 
+/* One layer of a chain of products (see bitnet_w2a8_chain). */
+typedef struct {
+    const uint8_t *packed;  /* device, tile layout of an N x K ternary matrix */
+    const float *scales;    /* device, tiled block scales */
+    int N, K;
+    int fold_input;         /* 0: input is the previous output [M][K]; 1: the previous output is
+                               [M][2K] and the input is h = prev[:, :K] + prev[:, K:] */
+} bitnet_chain_layer_t;
+
+/* Workspace bytes bitnet_w2a8_chain needs for these layers at batch M (0 if the
+ * chain is invalid): two fp32 [M][max N] activation buffers, int8 [M][max K] and
+ * fp32 [M] for the quantised activations. */
+size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int n, int M);
+
+/* Decode pass through a stack of n W2A8 linear layers: layer i quantises its
+ * input per token exactly as bitnet_quant_act (or bitnet_quant_act_fold when
+ * fold_input) and multiplies as bitnet_w2a8_gemv; its fp32 output is the next
+ * layer's input.  This is the chained decode of a BitNet model's linear layers
+ * ([P2] "Architecture foundations": W2A8 products; [P3] "Why WASM": a 2.4B ternary
+ * model), with the fused gate+up output folded to the down-projection width
+ * (the plain linear reading of the junction).  One launch per layer when M <= 4.
+ *   layers     host array of n descriptors (device pointers inside)
+ *   x          device, [M][layers[0].K], xdt BITNET_DT_BF16 or BITNET_DT_F32
+ *   y          device, fp32 [M][layers[n-1].N] (out)
+ *   workspace  device, >= bitnet_w2a8_chain_workspace_bytes(layers, n, M), 256-byte aligned;
+ *              clobbered
+ * Rules: 1 <= M <= 16; each layer's shape follows the shape rules; K of layer i
+ * equals N of layer i-1 (or half of it when fold_input); layer 0 has fold_input 0.
+ * Enqueues everything on `stream` (capturable in a HIP graph); no allocation. */
+bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
+                                  float *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Exact integer product acc[m][n] = sum_k T[n][k] * Q[m][k] (int32, device, [M][N]),
  * computed by the same kernels as the two products above (M <= 16: the decode
  * kernel; larger M: the prefill kernel), so that their integer core can be

@@ -1,0 +1,136 @@
+"""GPU parity of the chained decode (a stack of W2A8 layers with per-token
+requantisation and the gate+up fold between them).
+
+Layer-local: every layer of the chain is compared with the oracle fed the
+GPU's own input to that layer (bit-exact int8 / factors, fp32 within the
+product tolerance).  The chain equals the products called one by one, bit for
+bit.  End to end over the full 30-layer stack only statistical agreement can
+hold, because the fp32 summation order differs from the oracle's fp64 and
+requantisation turns last-bit differences into occasional +-1 steps."""
+import numpy as np
+import pytest
+
+import bit_gemv_i2_amd as bn
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+RTOL = 1e-5
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# (N, K, fold): K of a folded layer is half the previous N
+SMALL = [(256, 512, False), (384, 256, False), (1024, 384, False), (384, 512, True), (128, 384, False)]
+
+
+def _small_chain(seed):
+    Ts, Ss, ws = [], [], []
+    for i, (N, K, f) in enumerate(SMALL):
+        r = wl.rng_for(71, seed, i)
+        T = wl.ternary_uniform(r, N, K)
+        S = wl.uniform_scales(r, N, K, div=np.sqrt(7 * K / 6))
+        Ts.append(T)
+        Ss.append(S)
+        ws.append(bn.PackedWeight.from_ternary(T, S))
+    return Ts, Ss, ws, [f for (_, _, f) in SMALL]
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_chain_layer_local_parity(gpu, M):
+    Ts, Ss, ws, folds = _small_chain(M)
+    xb = wl.normal_act(wl.rng_for(72, M), M, SMALL[0][1])
+    x = dev(xb.view(np.int16)).view(torch.bfloat16)
+    prev = None
+    for k in range(len(SMALL)):
+        y = host(bn.Chain(ws[:k + 1], folds[:k + 1])(x))
+        if k == 0:
+            q, s = oracle.quant_act_bf16(xb)
+        elif folds[k]:
+            q, s = oracle.fold_quant(prev)
+        else:
+            q, s = oracle.quant_act_f32(prev)
+        N, K, _ = SMALL[k]
+        ref = oracle.w2a8(oracle.pack_i2s(Ts[k]), Ss[k], q, s, N, K)
+        bound = RTOL * np.maximum(np.abs(ref["y64"]), ref["mag"])
+        assert np.all(np.abs(y.astype(np.float64) - ref["y64"]) <= bound), f"layer {k}"
+        prev = y
+
+
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_chain_equals_products_called_one_by_one(gpu, M):
+    Ts, Ss, ws, folds = _small_chain(10 + M)
+    xb = wl.normal_act(wl.rng_for(73, M), M, SMALL[0][1])
+    x = dev(xb.view(np.int16)).view(torch.bfloat16)
+    y_chain = host(bn.Chain(ws, folds)(x))
+    h = x
+    for w, f in zip(ws, folds):
+        if M <= 4:
+            h = bn.bitnet_w2a8_gemv_act(w.packed, w.scales, h, w.N, w.K, fold=f)
+        else:
+            q, s = bn.bitnet_quant_act_fold(h) if f else bn.bitnet_quant_act(h)
+            h = bn.bitnet_w2a8_gemv(w.packed, w.scales, q, s, w.N, w.K)
+    assert np.array_equal(y_chain.view(np.uint32), host(h).view(np.uint32))
+
+
+def test_chain_rejects_mismatched_shapes(gpu):
+    Ts, Ss, ws, folds = _small_chain(3)
+    x = torch.zeros((1, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bn.BitnetError):
+        bn.Chain([ws[0], ws[2]], [False, False])(x)      # K of layer 1 != N of layer 0
+    with pytest.raises(bn.BitnetError):
+        bn.Chain(ws[:4], [False, False, False, False])(x)  # the fold is missing
+    with pytest.raises(bn.BitnetError):
+        bn.Chain(ws[:1], [True])(x)                        # layer 0 cannot fold
+
+
+def _oracle_chain(oracle_layers, folds, xb):
+    """The oracle run through the chain from its own outputs (fp64 values rounded
+    to fp32 between layers)."""
+    h = None
+    for i, (P, S, (N, K)) in enumerate(oracle_layers):
+        if i == 0:
+            q, s = oracle.quant_act_bf16(xb)
+        elif folds[i]:
+            q, s = oracle.fold_quant(h)
+        else:
+            q, s = oracle.quant_act_f32(h)
+        h = oracle.w2a8(P, S, q, s, N, K)["y"]
+    return h
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M,layers", [(1, 30), (8, 4)])
+def test_full_stack_end_to_end_statistical(gpu, M, layers):
+    """Requantisation is discontinuous: a difference far below one int8 step
+    flips a fraction ~127*|e|/amax of the codes by a whole step, so two exact
+    evaluations of a deep chain that differ only in fp32 rounding order drift
+    apart until they differ by quantisation noise.  The GPU chain must stay
+    within a small multiple of the oracle's own drift under a one-ulp
+    perturbation of the input."""
+    ws, folds, oracle_layers = [], [], []
+    for layer in range(layers):
+        for idx in range(6):
+            T, S = wl.stack_matrix(layer, idx)
+            ws.append(bn.PackedWeight.from_ternary(T, S))
+            folds.append(idx == 5)
+            oracle_layers.append((oracle.pack_i2s(T), S, T.shape))
+    xb = wl.stack_input(M)
+    y = host(bn.Chain(ws, folds)(dev(xb.view(np.int16)).view(torch.bfloat16)))
+    yo = _oracle_chain(oracle_layers, folds, xb)
+    xp = xb.copy()
+    xp[:, ::64] += np.uint16(1)  # one bf16 ulp on 1/64 of the inputs
+    yp = _oracle_chain(oracle_layers, folds, xp)
+    rel = float(np.linalg.norm(y - yo) / np.linalg.norm(yo))
+    rel_ref = float(np.linalg.norm(yp - yo) / np.linalg.norm(yo))
+    print(f"stack M={M} layers={layers}: GPU vs oracle rel L2 {rel:.3e}; oracle vs perturbed oracle {rel_ref:.3e}")
+    assert np.all(np.isfinite(y))
+    assert rel <= 3.0 * rel_ref + 1e-6
