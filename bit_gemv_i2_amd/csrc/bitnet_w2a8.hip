@@ -513,14 +513,25 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 }
 
 // ==========================================================================
-// a6: prefill product, any M.  Workgroup = 4 waves (2 x 2) on a 128-token x
-// 128-row output tile; each wave owns 64 tokens x 64 rows = 4 x 4 matrix-core
-// tiles.  Per 128-weight block a wave decodes its 4 row-tiles once (8 words
-// per lane) and reuses them for its 4 token-tiles (32 matrix-core steps),
-// then drains the int32 tiles into fp32 with the block scales.  The next
-// block's operands are loaded while the current one computes.
+// a6: prefill product, any M.  A 512-thread workgroup owns a 128-token x
+// 256-row output tile; wave (wm, wn) = (w / 4, w % 4) owns 64 tokens x 64 rows
+// = 4 x 4 matrix-core tiles.  Per 128-weight block the workgroup stages the
+// block's activations (128 x 128 int8, rows padded to 144 bytes so the
+// operand reads are conflict-free), its 16 packed bricks (8 KB) and 256
+// scales in LDS with two or three coalesced 16-byte loads per thread; the
+// next block's loads are in flight while the current block computes (double
+// buffer, one barrier per block).  Each wave decodes its 4 row-tiles once per
+// block and reuses them for its 4 token-tiles (32 matrix-core steps), then
+// drains the int32 tiles into fp32 with the block scales.  Workgroups are
+// ordered so that the token tiles sharing a weight tile run on one XCD (one
+// L2) when the grid divides evenly over the 8 XCDs.
 // ==========================================================================
-constexpr int kGemmBM = 128, kGemmBN = 128;
+constexpr int kGemmBM = 128, kGemmBN = 256, kGemmThreads = 512;
+constexpr int kAStride = 144;                        // padded LDS row of the activation tile
+constexpr int kAStage = kGemmBM * kAStride;          // 18432 bytes
+constexpr int kBStage = (kGemmBN / 16) * 512;        // 8192 bytes: 16 bricks
+constexpr int kSStage = kGemmBN * 4;                 // 1024 bytes: [row j][16 tiles] fp32
+constexpr int kStage = kAStage + kBStage + kSStage;  // 27648 bytes
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -529,29 +540,67 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 template <int OUT>  // 0: bf16 y, 1: fp32 y, 2: int32 acc
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ packed,
-                                                    const float *__restrict__ scales,
-                                                    const int8_t *__restrict__ q,
-                                                    const float *__restrict__ s_a, void *__restrict__ yout,
-                                                    int M, int N, int K) {
-    const int nblk = K >> 7;
-    const int ntile_n = N >> 4;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, j = l & 15;
-    const int tm0 = blockIdx.y * kGemmBM + (w >> 1) * 64;  // first token of this wave
-    const int tt0 = blockIdx.x * (kGemmBN / 16) + (w & 1) * 4;  // first row-tile of this wave
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ packed,
+                                                             const float *__restrict__ scales,
+                                                             const int8_t *__restrict__ q,
+                                                             const float *__restrict__ s_a, void *__restrict__ yout,
+                                                             int M, int N, int K, int ntm) {
+    __shared__ __align__(16) unsigned char lds[2 * kStage];
+    const int G = gridDim.x;
+    int t = blockIdx.x;
+    if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // XCD-aware order
+    const int tm = t % ntm, tn = t / ntm;
+    const int m0 = tm * kGemmBM, T0 = tn * (kGemmBN / 16);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, g = l >> 4, j = l & 15;
+    const int wm = w >> 2, wn = w & 3;
+    const int nblk = K >> 7, ntile_n = N >> 4;
 
-    // per-lane sources
-    const int8_t *qp[4];
-    bool qok[4];
+    // staging assignment (global -> registers -> LDS)
+    int arow[2], acol[2];
+    const int8_t *aptr[2];
+    bool aok[2];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-        const int tokn = tm0 + 16 * ti + j;
-        qok[ti] = tokn < M;
-        qp[ti] = q + (size_t)(qok[ti] ? tokn : 0) * K + g * 16;
+    for (int r = 0; r < 2; ++r) {
+        const int c = tid + kGemmThreads * r;
+        arow[r] = c >> 3;
+        acol[r] = (c & 7) * 16;
+        const int tok = m0 + arow[r];
+        aok[r] = tok < M;
+        aptr[r] = q + (size_t)(aok[r] ? tok : 0) * K + acol[r];
     }
-    bool rok[4];
+    const int bT = T0 + (tid >> 5);
+    const bool bok = bT < ntile_n;
+    const uint8_t *bptr = packed + (size_t)(bok ? bT : 0) * nblk * kBrickBytes + (tid & 31) * 16;
+    const int sT = T0 + (tid >> 2);
+    const bool sok = OUT != 2 && tid < 64 && sT < ntile_n;
+    const float *sptr = scales + (size_t)(sok ? sT : 0) * nblk * kTileN + (tid & 3) * 4;
+
+    // Two register sets of staged data: the loads of block b+2 are issued while
+    // block b computes and block b+1's data (issued one iteration earlier) is
+    // stored to LDS after it, so each block's load latency is covered by a
+    // full iteration plus a barrier.
+    struct Staged {
+        uint4 a[2];
+        uint4 b;
+        float4 s;
+    };
+    auto gload = [&](int b, Staged &r) {
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) rok[tj] = (tt0 + tj) < ntile_n;
+        for (int i = 0; i < 2; ++i)
+            r.a[i] = aok[i] ? *reinterpret_cast<const uint4 *>(aptr[i] + (size_t)b * kBlockK) : make_uint4(0, 0, 0, 0);
+        r.b = bok ? *reinterpret_cast<const uint4 *>(bptr + (size_t)b * kBrickBytes) : make_uint4(0, 0, 0, 0);
+        r.s = sok ? *reinterpret_cast<const float4 *>(sptr + (size_t)b * kTileN) : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto lstore = [&](int st, const Staged &r) {
+        unsigned char *base = lds + st * kStage;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(base + arow[i] * kAStride + acol[i]) = r.a[i];
+        *reinterpret_cast<uint4 *>(base + kAStage + tid * 16) = r.b;
+        if (OUT != 2 && tid < 64)  // [tile][16 rows], the global order of one block's scales
+            *reinterpret_cast<float4 *>(base + kAStage + kBStage + tid * 16) = r.s;
+    };
 
     float yacc[4][4][4];
     int iacc[4][4][4];
@@ -565,78 +614,101 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
                 iacc[a][b][e] = 0;
             }
 
-    v4i an[4][2];
-    uint2 wn[4];
-    float sn[4];
-    auto load_block = [&](int b, v4i (&aa)[4][2], uint2 (&ww)[4], float (&ss)[4]) {
+    auto compute = [&](int st) {
+        const unsigned char *base = lds + st * kStage;
+        v4i ao[4][2];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                aa[ti][s] = qok[ti] ? *reinterpret_cast<const v4i *>(qp[ti] + (size_t)b * kBlockK + s * 64)
-                                    : v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            const size_t brick = (size_t)(rok[tj] ? tt0 + tj : 0) * nblk + b;
-            ww[tj] = rok[tj] ? *reinterpret_cast<const uint2 *>(packed + brick * kBrickBytes + l * 8)
-                             : make_uint2(0u, 0u);
-            ss[tj] = (OUT != 2 && rok[tj]) ? scales[brick * kTileN + j] : 0.0f;
-        }
-    };
-    load_block(0, an, wn, sn);
-    for (int b = 0; b < nblk; ++b) {
-        v4i ac[4][2];
-        uint2 wc[4];
-        float sc[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            ac[ti][0] = an[ti][0];
-            ac[ti][1] = an[ti][1];
-        }
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            wc[tj] = wn[tj];
-            sc[tj] = sn[tj];
-        }
-        if (b + 1 < nblk) load_block(b + 1, an, wn, sn);
+                ao[ti][s] = *reinterpret_cast<const v4i *>(base + (64 * wm + 16 * ti + j) * kAStride + 64 * s + 16 * g);
         v4i bw[4][2];
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            bw[tj][0] = decode16(wc[tj].x);
-            bw[tj][1] = decode16(wc[tj].y);
+            const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + (4 * wn + tj) * 512 + l * 8);
+            bw[tj][0] = decode16(wv.x);
+            bw[tj][1] = decode16(wv.y);
         }
+        // matrix-core A = decoded weights (rows), B = activations (tokens): lane (g, j)
+        // receives rows 4g..4g+3 of token j, so the drain needs those 4 rows' scales
+        float sc[4][4];
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            if (OUT != 2) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(base + kAStage + kBStage +
+                                                                    ((4 * wn + tj) * 16 + 4 * g) * 4);
+                sc[tj][0] = s4.x;
+                sc[tj][1] = s4.y;
+                sc[tj][2] = s4.z;
+                sc[tj][3] = s4.w;
+            } else {
+                sc[tj][0] = sc[tj][1] = sc[tj][2] = sc[tj][3] = 0.0f;
+            }
+        }
+        // the 16 tiles' first K-steps are independent and pipeline on the matrix
+        // core; the second K-steps then find their accumulators long finished
+        v4i c[4][4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                v4i c = v4i{0, 0, 0, 0};
-                c = mfma_i8(ac[ti][0], bw[tj][0], c);
-                c = mfma_i8(ac[ti][1], bw[tj][1], c);
+            for (int tj = 0; tj < 4; ++tj) c[ti][tj] = mfma_i8(bw[tj][0], ao[ti][0], v4i{0, 0, 0, 0});
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) c[ti][tj] = mfma_i8(bw[tj][1], ao[ti][1], c[ti][tj]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (OUT == 2) iacc[ti][tj][e] += c[e];
-                    else yacc[ti][tj][e] = fmaf(sc[tj], (float)c[e], yacc[ti][tj][e]);
+                    if (OUT == 2) iacc[ti][tj][e] += c[ti][tj][e];
+                    else yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
                 }
-            }
+    };
+
+    Staged r0, r1;
+    gload(0, r0);
+    if (nblk > 1) gload(1, r1);
+    lstore(0, r0);
+    __syncthreads();
+    // iteration b: ring slot (b & 1) is free, slot ((b + 1) & 1) holds block b+1
+    auto iter = [&](int b, Staged &freed, Staged &next) {
+        if (b + 2 < nblk) gload(b + 2, freed);
+        compute(b & 1);
+        if (b + 1 < nblk) lstore((b + 1) & 1, next);
+        __syncthreads();
+    };
+    for (int b = 0; b < nblk; b += 2) {
+        iter(b, r0, r1);
+        if (b + 1 < nblk) iter(b + 1, r1, r0);
     }
 
-    // epilogue: lane (g, j), tile (ti, tj), element e -> token tm0+16ti+4g+e, row 16(tt0+tj)+j
+    // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j,
+    // row 16(T0+4wn+tj)+4g+e: four consecutive outputs of one token per store
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0; ti < 4; ++ti) {
+        const int m = m0 + 64 * wm + 16 * ti + j;
+        if (m >= M) continue;
+        const float f = (OUT == 2) ? 0.0f : s_a[m] * 0.015625f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = tm0 + 16 * ti + 4 * g + e;
-            if (m >= M) continue;
-            const float f = (OUT == 2) ? 0.0f : s_a[m] * 0.015625f;
-#pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                if (!rok[tj]) continue;
-                const size_t idx = (size_t)m * N + (size_t)(tt0 + tj) * 16 + j;
-                if (OUT == 0) static_cast<uint16_t *>(yout)[idx] = f32_to_bf16_rne(yacc[ti][tj][e] * f);
-                else if (OUT == 1) static_cast<float *>(yout)[idx] = yacc[ti][tj][e] * f;
-                else static_cast<int32_t *>(yout)[idx] = iacc[ti][tj][e] >> 6;
+        for (int tj = 0; tj < 4; ++tj) {
+            const int T = T0 + 4 * wn + tj;
+            if (T >= ntile_n) continue;
+            const size_t idx = (size_t)m * N + (size_t)T * 16 + 4 * g;
+            if (OUT == 0) {
+                const uint32_t lo = f32_to_bf16_rne(yacc[ti][tj][0] * f) | ((uint32_t)f32_to_bf16_rne(yacc[ti][tj][1] * f) << 16);
+                const uint32_t hi = f32_to_bf16_rne(yacc[ti][tj][2] * f) | ((uint32_t)f32_to_bf16_rne(yacc[ti][tj][3] * f) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(yout) + idx) = make_uint2(lo, hi);
+            } else if (OUT == 1) {
+                *reinterpret_cast<float4 *>(static_cast<float *>(yout) + idx) =
+                    make_float4(yacc[ti][tj][0] * f, yacc[ti][tj][1] * f, yacc[ti][tj][2] * f, yacc[ti][tj][3] * f);
+            } else {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(yout) + idx) =
+                    make_int4(iacc[ti][tj][0] >> 6, iacc[ti][tj][1] >> 6, iacc[ti][tj][2] >> 6, iacc[ti][tj][3] >> 6);
             }
         }
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -754,11 +826,11 @@ void quant_launch(const void *x, int M, int K, int8_t *q, float *s_a, hipStream_
 template <int OUT>
 void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float *sa, void *y, int M, int N, int K,
                  hipStream_t st) {
-    dim3 grid((N + kGemmBN - 1) / kGemmBN, (M + kGemmBM - 1) / kGemmBM), block(256);
-    hipLaunchKernelGGL((gemm_kernel<OUT>), grid, block, 0, st, p, s, q, sa, y, M, N, K);
+    const int ntm = (M + kGemmBM - 1) / kGemmBM, ntn = (N + kGemmBN - 1) / kGemmBN;
+    hipLaunchKernelGGL((gemm_kernel<OUT>), dim3(ntm * ntn), dim3(kGemmThreads), 0, st, p, s, q, sa, y, M, N, K, ntm);
 }
 
-bool gemm_grid_ok(int M) { return (M + kGemmBM - 1) / kGemmBM <= 65535; }
+bool gemm_grid_ok(int M) { return (int64_t)((M + kGemmBM - 1) / kGemmBM) * 65536 < ((int64_t)1 << 31); }
 
 }  // namespace
 
@@ -805,7 +877,7 @@ bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, con
 bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, const int8_t *q, const float *s_a,
                                  void *y, int ydt, int M, int N, int K, hipStream_t stream) {
     if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
-    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 4))
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
@@ -837,7 +909,7 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
 
 bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int32_t *acc, int M, int N, int K,
                                     hipStream_t stream) {
-    if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 4))
+    if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 16))
         return BITNET_ERR_INVALID_ARG;
     // the int32 accumulators hold 64 * sum: |64 * 127 * K| < 2^31
     if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M) || K > 262144) return BITNET_ERR_UNSUPPORTED_SHAPE;
