@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="short eager run for hardware-counter passes: a 64 MiB device copy (the byte-count "
-                         "calibration) and 64 launches each of the headline product and fused step")
+                         "calibration), 64 launches each of the headline product and fused step, 16 prefill products")
     return ap.parse_args()
 
 
@@ -308,7 +308,16 @@ def profile_run(torch, bn, wl):
     for i in range(64):
         d.fused(i)
     torch.cuda.synchronize()
-    log(f"profile run done: copy {n} B x3, gemv x64, fused x64 (rotation {d.rot.R})")
+    del d
+    c4 = wl.config4()
+    w4 = bn.PackedWeight.from_ternary(c4.T, c4.S)
+    x4 = torch.from_numpy(c4.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    q4, s4 = bn.bitnet_quant_act(x4)
+    y4 = torch.empty((c4.M, c4.N), dtype=torch.bfloat16, device="cuda")
+    for i in range(16):
+        w4.gemm(q4, s4, y=y4)
+    torch.cuda.synchronize()
+    log(f"profile run done: copy {n} B x3, gemv x64, fused x64, prefill 512x13824x2560 x16")
 
 
 def main():
