@@ -237,7 +237,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
 // matrix-core operands from the LDS copy.  Every workgroup derives bit-
 // identical q and s_a, so the result equals quant-then-product.  Workgroup 0
 // optionally writes q and s_a out.
-// MW = accumulator elements drained per lane (1, 2 or 4): with M <= 4 only
+// TOK = token capacity (1, 2, 4, 8, 16) of the instantiation, M <= TOK.  Lane
+// (g, j) drains elements e < MW = min(TOK, 4) (tokens 4g + e): with M <= 4 only
 // tokens 0..M-1 (lanes 0..15, elements < M) carry data.
 // ==========================================================================
 struct GemvArgs {
@@ -254,8 +255,13 @@ struct GemvArgs {
 
 // LDS of the fused forms: [int8 copy of q, M*K bytes padded | reduction reuse]
 // then 16 fp32 dequant factors.
+// Row stride of the LDS copy of q: K plus 16 bytes, so that the token rows read
+// together by one matrix-core operand load start 4 banks apart (K is a multiple
+// of 128 bytes and would put every row on the same banks).
+__host__ __device__ inline int lds_qstride(int K) { return K + 16; }
+
 __host__ __device__ inline size_t gemv_fused_region(int M, int K, int nwc) {
-    const size_t qbytes = ((size_t)M * K + 15) & ~(size_t)15;
+    const size_t qbytes = (size_t)M * lds_qstride(K);
     const size_t red = (size_t)nwc * 4 * 64 * sizeof(int);
     return qbytes > red ? qbytes : red;
 }
@@ -284,7 +290,7 @@ __device__ void quant_wave(const GemvArgs &args, int8_t *qs, float *sa_lds, int 
                 const int c = c0 + u * kWave + l;
                 if (c < nvec) {
                     const uint2 qv = quantize8(f[u], inv);
-                    *reinterpret_cast<uint2 *>(qs + (size_t)m * K + 8 * c) = qv;
+                    *reinterpret_cast<uint2 *>(qs + (size_t)m * lds_qstride(K) + 8 * c) = qv;
                     if (args.q_out && blockIdx.x == 0)
                         *reinterpret_cast<uint2 *>(args.q_out + (size_t)m * K + 8 * c) = qv;
                 }
@@ -307,8 +313,9 @@ enum GemvForm {
     kQuantWaves = 4 // fused quantisation by 4 extra quant waves (4 < M <= 16)
 };
 
-template <int AM, int NB, int MW, bool INT_OUT, int FORM>
+template <int AM, int NB, int TOK, bool INT_OUT, int FORM>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
+    constexpr int MW = TOK < 4 ? TOK : 4;  // accumulator elements drained per lane
     extern __shared__ __align__(16) unsigned char smem[];
     const int M = args.M, N = args.N, K = args.K, per = args.per, nwc = args.nwc;
     const int nblk = K >> 7;
@@ -355,9 +362,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
             for (int r = 0; r < (FORM == kAllWaves ? CR : 1); ++r)
                 xr[m][r] = load_raw8<XM>(args.act, min(m, M - 1), K, bw0 * 16 + min(l + kWave * r, nchw - 1));
     }
-    // kStaged: this wave's K-slice of q for M <= MW tokens in 16-byte chunks
-    constexpr int QR = (MW * NB + 7) / 8;
-    uint4 qraw[FORM == kStaged ? QR : 1];
+    // kStaged: this wave's K-slice of q for M <= TOK tokens in 16-byte chunks
+    constexpr int QR = (TOK * NB + 7) / 8;
+    v4i qraw[FORM == kStaged ? QR : 1];  // native vector: a register value, not an aggregate
     const int qper = nbw * 8;  // chunks per token
     if (FORM == kStaged) {
         const int8_t *q = static_cast<const int8_t *>(args.act);
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
         for (int r = 0; r < (FORM == kStaged ? QR : 1); ++r) {
             const int c = min(l + kWave * r, M * qper - 1);
             const int m = c / qper, o = c - m * qper;
-            qraw[r] = *reinterpret_cast<const uint4 *>(q + (size_t)m * K + (size_t)bw0 * kBlockK + 16 * o);
+            qraw[r] = *reinterpret_cast<const v4i *>(q + (size_t)m * K + (size_t)bw0 * kBlockK + 16 * o);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
                 const int c = l + kWave * r;
                 if (c < M * qper) {
                     const int m = c / qper, o = c - m * qper;
-                    *reinterpret_cast<uint4 *>(qs + (size_t)m * K + (size_t)bw0 * kBlockK + 16 * o) = qraw[r];
+                    *reinterpret_cast<v4i *>(qs + (size_t)m * lds_qstride(K) + (size_t)bw0 * kBlockK + 16 * o) = qraw[r];
                 }
             }
             // the wave reads back only its own slice: LDS keeps one wave's accesses in order
@@ -432,9 +439,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
                     const int c = l + kWave * r;
                     if (c < nchw) {
                         const uint2 qv = quantize8(xf[m][r], inv);
-                        const size_t off = (size_t)m * K + (size_t)bw0 * kBlockK + 8 * c;
-                        *reinterpret_cast<uint2 *>(qs + off) = qv;
-                        if (args.q_out && blockIdx.x == 0) *reinterpret_cast<uint2 *>(args.q_out + off) = qv;
+                        const size_t off = (size_t)bw0 * kBlockK + 8 * c;
+                        *reinterpret_cast<uint2 *>(qs + (size_t)m * lds_qstride(K) + off) = qv;
+                        if (args.q_out && blockIdx.x == 0)
+                            *reinterpret_cast<uint2 *>(args.q_out + (size_t)m * K + off) = qv;
                     }
                 }
                 if (w == 0 && l == 0) {
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
         } else if constexpr (FORM == kQuantWaves) {
             lds_barrier();  // q ready (written by the quant waves)
         }
-        const int8_t *qp = qsrc + (size_t)j * K + (size_t)c0 * kBlockK + g * 16;
+        const int8_t *qp = qsrc + (size_t)j * (LDSQ ? lds_qstride(K) : K) + (size_t)c0 * kBlockK + g * 16;
         v4i a[NB][2];
 #pragma unroll
         for (int i = 0; i < NB; ++i)
@@ -720,25 +728,41 @@ bitnet_status_t launched() {
     return hipGetLastError() == hipSuccess ? BITNET_OK : BITNET_ERR_HIP;
 }
 
+// The all-waves fused form keeps every token's raw activation chunks in registers
+// until the weights are in flight: tokens x chunk rounds x 16-byte words per chunk
+// must stay within 64 dwords (more spills).
+__host__ __device__ constexpr bool allwaves_fits(int xm, int tok, int nb) {
+    return tok * ((nb + 3) / 4) * (xm == 0 ? 4 : xm == 1 ? 8 : 16) <= 64;
+}
+
 template <int AM, int NB, bool INT_OUT, int FORM>
-void gemv_launch_mw(int mw, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
-    if (FORM == kQuantWaves || INT_OUT || mw == 4)
-        hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, INT_OUT, FORM>), grid, block, lds, st, a);
-    else if (mw == 2)
-        hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, INT_OUT, FORM>), grid, block, lds, st, a);
-    else
-        hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, INT_OUT, FORM>), grid, block, lds, st, a);
+void gemv_launch_tok(int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
+    if constexpr (FORM == kAllWaves) {  // M <= 4 and allwaves_fits (checked by the caller)
+        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, false, FORM>), grid, block, lds, st, a);
+        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, false, FORM>), grid, block, lds, st, a);
+        else if constexpr (allwaves_fits(AM < 0 ? 0 : AM, 4, NB))
+            hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, false, FORM>), grid, block, lds, st, a);
+    } else if constexpr (FORM == kStaged) {
+        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, INT_OUT, FORM>), grid, block, lds, st, a);
+        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, INT_OUT, FORM>), grid, block, lds, st, a);
+        else if (tok == 4) hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, INT_OUT, FORM>), grid, block, lds, st, a);
+        else if (tok == 8) hipLaunchKernelGGL((gemv_kernel<AM, NB, 8, INT_OUT, FORM>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, INT_OUT, FORM>), grid, block, lds, st, a);
+    } else {  // kDirect, kMulti, kQuantWaves: token capacity 16
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, (FORM == kQuantWaves ? false : INT_OUT), FORM>), grid, block, lds,
+                           st, a);
+    }
 }
 
 template <int AM, int NB, bool INT_OUT>
-void gemv_launch_form(int form, int mw, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
+void gemv_launch_form(int form, int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
     if constexpr (AM >= 0) {
-        if (form == kQuantWaves) gemv_launch_mw<AM, NB, false, kQuantWaves>(mw, grid, block, lds, st, a);
-        else gemv_launch_mw<AM, NB, false, kAllWaves>(mw, grid, block, lds, st, a);
+        if (form == kQuantWaves) gemv_launch_tok<AM, NB, false, kQuantWaves>(tok, grid, block, lds, st, a);
+        else gemv_launch_tok<AM, NB, false, kAllWaves>(tok, grid, block, lds, st, a);
     } else {
-        if (form == kStaged) gemv_launch_mw<AM, NB, INT_OUT, kStaged>(mw, grid, block, lds, st, a);
-        else if (NB == 8 && form == kMulti) gemv_launch_mw<AM, 8, INT_OUT, kMulti>(mw, grid, block, lds, st, a);
-        else gemv_launch_mw<AM, NB, INT_OUT, kDirect>(mw, grid, block, lds, st, a);
+        if (form == kStaged) gemv_launch_tok<AM, NB, INT_OUT, kStaged>(tok, grid, block, lds, st, a);
+        else if (NB == 8 && form == kMulti) gemv_launch_tok<AM, 8, INT_OUT, kMulti>(tok, grid, block, lds, st, a);
+        else gemv_launch_tok<AM, NB, INT_OUT, kDirect>(tok, grid, block, lds, st, a);
     }
 }
 
@@ -768,6 +792,16 @@ void gemv_split(int K, int *nw_out, int *per_out) {
 
 size_t gemv_fused_lds(int M, int K, int nw) { return gemv_fused_region(M, K, nw) + (16 + 48) * sizeof(float); }
 
+// Form of the fused quantise-and-multiply launch for activation mode xm (0 bf16,
+// 1 fp32, 2 folded fp32): every compute wave quantises its own slice when the
+// tokens' raw chunks fit in registers, else four extra quant waves do it.
+int gemv_fused_form(int xm, int M, int K) {
+    int nw, per;
+    gemv_split(K, &nw, &per);
+    const int tok = M == 1 ? 1 : M == 2 ? 2 : 4;
+    return (M <= 4 && allwaves_fits(xm, tok, per < 8 ? per : 8)) ? kAllWaves : kQuantWaves;
+}
+
 // Picks the form and launches.  Returns false (nothing launched) if a fused
 // form was asked for and does not fit.
 template <int AM, bool INT_OUT>
@@ -780,7 +814,7 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
     size_t lds;
     if (AM >= 0) {
         if (per > 8) return false;
-        form = a.M <= 4 ? kAllWaves : kQuantWaves;
+        form = gemv_fused_form(AM, a.M, a.K);
         a.qw = form == kQuantWaves ? 4 : 0;
         lds = gemv_fused_lds(a.M, a.K, nw);
         if (lds > kMaxLds) return false;
@@ -789,7 +823,7 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
         if (per > 8) {
             form = kMulti;
             lds = (size_t)nw * 4 * kWave * sizeof(int);
-        } else if (a.M <= 4 && gemv_fused_lds(a.M, a.K, nw) <= kMaxLds) {
+        } else if (gemv_fused_lds(a.M, a.K, nw) <= kMaxLds) {
             form = kStaged;
             lds = gemv_fused_lds(a.M, a.K, nw);
         } else {
@@ -798,17 +832,17 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
         }
     }
     const int nb = per < 8 ? per : 8;
-    const int mw = a.M == 1 ? 1 : (a.M == 2 ? 2 : 4);
+    const int tok = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     dim3 grid(a.N / (int)kTileN), block(kWave * (nw + a.qw));
     switch (nb) {
-        case 1: gemv_launch_form<AM, 1, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 2: gemv_launch_form<AM, 2, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 3: gemv_launch_form<AM, 3, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 4: gemv_launch_form<AM, 4, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 5: gemv_launch_form<AM, 5, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 6: gemv_launch_form<AM, 6, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        case 7: gemv_launch_form<AM, 7, INT_OUT>(form, mw, grid, block, lds, st, a); break;
-        default: gemv_launch_form<AM, 8, INT_OUT>(form, mw, grid, block, lds, st, a); break;
+        case 1: gemv_launch_form<AM, 1, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 2: gemv_launch_form<AM, 2, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 3: gemv_launch_form<AM, 3, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 4: gemv_launch_form<AM, 4, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 5: gemv_launch_form<AM, 5, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 6: gemv_launch_form<AM, 6, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 7: gemv_launch_form<AM, 7, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        default: gemv_launch_form<AM, 8, INT_OUT>(form, tok, grid, block, lds, st, a); break;
     }
     return true;
 }
@@ -990,7 +1024,9 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
         const int dt = L.fold_input ? BITNET_DT_F32_FOLD2 : in_dt;
         int nw, per;
         gemv_split(L.K, &nw, &per);
-        const bool fused = M <= 4 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds;
+        // one launch when the cheap fused form applies, else quantise + multiply
+        const bool fused = per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
+                           gemv_fused_form(dt == BITNET_DT_BF16 ? 0 : dt == BITNET_DT_F32 ? 1 : 2, M, L.K) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
             bool ok;

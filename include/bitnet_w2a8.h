@@ -168,7 +168,7 @@ bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, con
  *   q_out    device, int8 [M][K] (out, optional: NULL to skip)
  *   s_a_out  device, fp32 [M] (out, optional: NULL to skip)
  *   packed, scales as bitnet_w2a8_gemv.
- * Rules: 1 <= M <= 16, the shape rules, K <= 12288 and M*K <= 64512 (the int8
+ * Rules: 1 <= M <= 16, the shape rules, K <= 12288 and M*(K+16) <= 65280 (the int8
  * copy of the activations lives in LDS); otherwise BITNET_ERR_UNSUPPORTED_SHAPE
  * and the caller uses bitnet_quant_act + bitnet_w2a8_gemv. */
 bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales, const void *x, int xdt,
