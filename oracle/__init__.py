@@ -43,6 +43,7 @@ def _load():
             "oracle_acc_dense": [p, p, i64, i64, i64, p],
             "oracle_f32_to_bf16": [p, i64, p],
             "oracle_fold_quant": [p, i64, i64, p, p, p],
+            "oracle_glu_quant": [p, i64, i64, p, p, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -158,4 +159,16 @@ def fold_quant(y):
     s = np.empty((M,), np.float32)
     scratch = np.empty((M, H), np.float32)
     _check(_load().oracle_fold_quant(_ptr(y), M, H, _ptr(q), _ptr(s), _ptr(scratch)), "fold_quant")
+    return q, s
+
+
+def glu_quant(y):
+    """y fp32 [M][2H] (gate | up) -> h = relu(gate)^2 * up -> (q int8 [M][H], s_a fp32 [M])."""
+    y = _c(y, np.float32)
+    M, H2 = y.shape
+    H = H2 // 2
+    q = np.empty((M, H), np.int8)
+    s = np.empty((M,), np.float32)
+    scratch = np.empty((M, H), np.float32)
+    _check(_load().oracle_glu_quant(_ptr(y), M, H, _ptr(q), _ptr(s), _ptr(scratch)), "glu_quant")
     return q, s

@@ -266,3 +266,28 @@ int oracle_fold_quant(const float *y, int64_t M, int64_t H, int8_t *q, float *s_
         }
     return oracle_quant_act_f32(scratch, M, H, q, s_a);
 }
+
+/* ------------------------------------------------------------------------ */
+/* a7 variant: squared-ReLU gated junction.                                   */
+/* [P4] "BitRun v0.2 measured", section "Architecture-specific SIMD           */
+/* acceleration": the runtime pairs its ternary dot-product kernels with a    */
+/* squared-ReLU activation.  Reading: the fused gate+up output y [M][2H]      */
+/* carries the gate in its first H columns and the up projection in the      */
+/* last H; the next layer's input is h = relu(gate)^2 * up, evaluated in fp32 */
+/* as r = max(gate, 0), then (r * r), then that times up (two roundings, no   */
+/* fused multiply-add), then re-quantised per token as in a4.                 */
+/* ------------------------------------------------------------------------ */
+int oracle_glu_quant(const float *y, int64_t M, int64_t H, int8_t *q, float *s_a, float *scratch)
+{
+    if (M <= 0 || H <= 0) return -1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < H; ++j) {
+            const float gate = y[m * 2 * H + j];
+            const float up = y[m * 2 * H + H + j];
+            const float r = gate > 0.0f ? gate : 0.0f;
+            volatile float r2 = r * r;
+            volatile float h = r2 * up;
+            scratch[m * H + j] = h;
+        }
+    return oracle_quant_act_f32(scratch, M, H, q, s_a);
+}

@@ -322,3 +322,56 @@ def test_fold_quant_closed_form():
     assert q[0, 3] == 127 and q[0, 10] == int(np.rint(np.float32(-1.5) * (np.float32(127) / np.float32(3))))
     assert s[0] == np.float32(np.float32(3.0) / np.float32(127))
     assert np.count_nonzero(q) == 2
+
+
+# Squared-ReLU gated junction: h = relu(gate)^2 * up (gate = first half).
+def test_glu_quant_unit_gate_is_plain_quant():
+    # gate = 1 -> relu(1)^2 = 1 exactly, so h = up and the junction reduces to
+    # the plain per-token quantiser (pinned above against numpy fp32)
+    rng = np.random.default_rng(41)
+    M, H = 3, 384
+    up = rng.standard_normal((M, H)).astype(np.float32)
+    y = np.concatenate([np.ones((M, H), np.float32), up], axis=1)
+    q, s = oracle.glu_quant(y)
+    q0, s0 = oracle.quant_act_f32(up)
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    # halves swapped would read relu(up)^2 * 1: different codes
+    qs, _ = oracle.glu_quant(np.concatenate([up, np.ones((M, H), np.float32)], axis=1))
+    assert not np.array_equal(qs, q0)
+
+
+def test_glu_quant_integer_gates_exact_squares():
+    # integer gates, unit up: h is exactly relu(k)^2 (small integers are exact in fp32)
+    H = 128
+    k = np.tile(np.arange(-5, 12, dtype=np.float32), 8)[:H]
+    y = np.concatenate([k, np.ones(H, np.float32)])[None, :]
+    h_exact = np.where(k > 0, k * k, 0).astype(np.float32)[None, :]
+    q, s = oracle.glu_quant(y)
+    q0, s0 = oracle.quant_act_f32(h_exact)
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    assert s[0] == np.float32(np.float32(121.0) / np.float32(127.0))  # amax = 11^2
+    assert q[0, list(k).index(11.0)] == 127 and np.all(q[0, k <= 0] == 0)
+
+
+def test_glu_quant_negative_gate_and_symmetries():
+    rng = np.random.default_rng(42)
+    M, H = 2, 256
+    g = rng.standard_normal((M, H)).astype(np.float32)
+    u = rng.standard_normal((M, H)).astype(np.float32)
+    # gate <= 0 everywhere -> h = 0 -> q = 0, s_a = 1e-5/127
+    q, s = oracle.glu_quant(np.concatenate([-np.abs(g), u], axis=1))
+    assert not np.any(q) and np.all(s == np.float32(np.float32(1e-5) / np.float32(127)))
+    q, s = oracle.glu_quant(np.concatenate([g, u], axis=1))
+    # up -> -up negates the codes (relu applies to the gate only)
+    qn, sn = oracle.glu_quant(np.concatenate([g, -u], axis=1))
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # gate x 2 scales h by 4, up x 2 by 2: codes unchanged, factors scale exactly
+    q4, s4 = oracle.glu_quant(np.concatenate([2 * g, u], axis=1))
+    assert np.array_equal(q4, q) and np.array_equal(s4, 4 * s)
+    q2, s2 = oracle.glu_quant(np.concatenate([g, 2 * u], axis=1))
+    assert np.array_equal(q2, q) and np.array_equal(s2, 2 * s)
+    # a gate flipped negative zeroes exactly its own outputs
+    g2 = g.copy()
+    g2[:, :64] = -np.abs(g2[:, :64])
+    qz, _ = oracle.glu_quant(np.concatenate([g2, u], axis=1))
+    assert not np.any(qz[:, :64])
