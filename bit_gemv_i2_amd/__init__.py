@@ -19,7 +19,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitnet_w2a8.so")
 
 BITNET_OK, BITNET_ERR_INVALID_ARG, BITNET_ERR_UNSUPPORTED_SHAPE, BITNET_ERR_HIP = 0, 1, 2, 3
-BITNET_DT_BF16, BITNET_DT_F32, BITNET_DT_F32_FOLD2 = 0, 1, 2
+BITNET_DT_BF16, BITNET_DT_F32, BITNET_DT_F32_FOLD2, BITNET_DT_F32_RELU2_GLU = 0, 1, 2, 3
+BITNET_JUNCTION_NONE, BITNET_JUNCTION_SUM, BITNET_JUNCTION_RELU2_GLU = 0, 1, 2
+_JUNCTIONS = {False: 0, None: 0, "none": 0, True: 1, "sum": 1, "relu2_glu": 2, 0: 0, 1: 1, 2: 2}
+
+
+def junction_code(j) -> int:
+    """Junction of a two-half input: False/None/"none" -> 0, True/"sum" -> 1 (lo + hi),
+    "relu2_glu" -> 2 (relu(lo)^2 * hi); the integers 0..2 map to themselves."""
+    try:
+        return _JUNCTIONS[j]
+    except (KeyError, TypeError):
+        raise ValueError(f"unknown junction {j!r}") from None
 BLOCK_K = 128
 TILE_N = 16
 GEMV_MAX_M = 16
@@ -50,6 +61,8 @@ _SIGS = {
                           ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "bitnet_quant_act_fold": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p], ctypes.c_int),
+    "bitnet_quant_act_relu2_glu": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemv": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemm": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemv_act": ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3
@@ -199,8 +212,7 @@ def bitnet_quant_act(x, q=None, s_a=None, stream=None):
     return q, s_a
 
 
-def bitnet_quant_act_fold(y, q=None, s_a=None, stream=None):
-    """y: device fp32 [M][2H] -> h = y[:, :H] + y[:, H:] quantised: (q int8 [M][H], s_a fp32 [M])."""
+def _quant_two_half(name, y, q, s_a, stream):
     import torch
     M, H2 = y.shape
     H = H2 // 2
@@ -210,9 +222,18 @@ def bitnet_quant_act_fold(y, q=None, s_a=None, stream=None):
         q = torch.empty((M, H), dtype=torch.int8, device=y.device)
     if s_a is None:
         s_a = torch.empty((M,), dtype=torch.float32, device=y.device)
-    _ok(lib().bitnet_quant_act_fold(_dev_ptr(y, "y"), M, H, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"),
-                                    _stream(stream)), "bitnet_quant_act_fold")
+    _ok(getattr(lib(), name)(_dev_ptr(y, "y"), M, H, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"), _stream(stream)), name)
     return q, s_a
+
+
+def bitnet_quant_act_fold(y, q=None, s_a=None, stream=None):
+    """y: device fp32 [M][2H] -> h = y[:, :H] + y[:, H:] quantised: (q int8 [M][H], s_a fp32 [M])."""
+    return _quant_two_half("bitnet_quant_act_fold", y, q, s_a, stream)
+
+
+def bitnet_quant_act_relu2_glu(y, q=None, s_a=None, stream=None):
+    """y: device fp32 [M][2H] (gate | up) -> h = relu(gate)^2 * up quantised: (q int8 [M][H], s_a fp32 [M])."""
+    return _quant_two_half("bitnet_quant_act_relu2_glu", y, q, s_a, stream)
 
 
 def bitnet_w2a8_gemv(packed, scales, q, s_a, N: int, K: int, y=None, stream=None):
@@ -230,14 +251,16 @@ def bitnet_w2a8_gemv(packed, scales, q, s_a, N: int, K: int, y=None, stream=None
 def bitnet_w2a8_gemv_act(packed, scales, x, N: int, K: int, fold: bool = False, y=None, q_out=None,
                          s_a_out=None, stream=None):
     """Decode step in one launch: quantise x (bf16/fp32 [M][K], or fp32 [M][2K]
-    folded when fold=True) and multiply.  Optional q_out / s_a_out receive the
-    int8 activations and dequant factors.  Returns y fp32 [M][N]."""
+    brought to width K by a junction: fold=True or "sum" for lo + hi,
+    "relu2_glu" for relu(lo)^2 * hi) and multiply.  Optional q_out / s_a_out
+    receive the int8 activations and dequant factors.  Returns y fp32 [M][N]."""
     import torch
     M = x.shape[0]
-    if fold:
+    jc = junction_code(fold)
+    if jc:
         if x.dtype != torch.float32 or x.shape[1] != 2 * K:
-            raise ValueError("fold needs fp32 x of shape [M][2K]")
-        xdt = BITNET_DT_F32_FOLD2
+            raise ValueError("a junction needs fp32 x of shape [M][2K]")
+        xdt = BITNET_DT_F32_FOLD2 if jc == BITNET_JUNCTION_SUM else BITNET_DT_F32_RELU2_GLU
     else:
         xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
         if xdt is None or x.shape[1] != K:
@@ -310,12 +333,13 @@ class PackedWeight:
 # ------------------------------------------------------------------ chained decode
 class Chain:
     """A stack of W2A8 layers run by bitnet_w2a8_chain.  `weights` are
-    PackedWeight objects; `folds[i]` marks a layer whose input is the previous
-    output folded in half (h = lo + hi)."""
+    PackedWeight objects; `folds[i]` is the junction in front of layer i
+    (False: none; True or "sum": previous output folded h = lo + hi;
+    "relu2_glu": h = relu(lo)^2 * hi)."""
 
     def __init__(self, weights, folds=None):
         self.weights = list(weights)
-        self.folds = [False] * len(self.weights) if folds is None else [bool(f) for f in folds]
+        self.folds = [0] * len(self.weights) if folds is None else [junction_code(f) for f in folds]
         n = len(self.weights)
         self._arr = (ChainLayer * n)()
         for i, (w, f) in enumerate(zip(self.weights, self.folds)):

@@ -59,7 +59,9 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 // folded, h = lo + hi (one fp32 addition, the junction of a stacked chain).
 // load8 reads values 8v .. 8v+7 of token m, widened exactly to fp32.
 // ==========================================================================
-// The raw 16-byte words behind 8 values (bf16: one, fp32: two, folded fp32: four),
+// Activation modes XM: 0 bf16, 1 fp32, 2 fp32 [2K] folded as lo + hi, 3 fp32 [2K]
+// gated as relu(lo)^2 * hi (the two junctions of a stacked decode chain).
+// The raw 16-byte words behind 8 values (bf16: one, fp32: two, two-half fp32: four),
 // so that loads can be issued early and converted only when their data is needed.
 template <int XM>
 struct Raw8 {
@@ -106,11 +108,19 @@ __device__ __forceinline__ void cvt8(const Raw8<XM> &r, float out[8]) {
         words8(r.u[0], r.u[1], w);
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(w[i]);
-        if constexpr (XM == 2) {
+        if constexpr (XM == 2) {  // linear junction: lo + hi
             uint32_t h[8];
             words8(r.u[2], r.u[3], h);
 #pragma unroll
             for (int i = 0; i < 8; ++i) out[i] = __fadd_rn(out[i], __uint_as_float(h[i]));
+        } else if constexpr (XM == 3) {  // squared-ReLU gate: (max(lo, 0)^2) * hi, two fp32 roundings
+            uint32_t h[8];
+            words8(r.u[2], r.u[3], h);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float g = out[i] > 0.0f ? out[i] : 0.0f;
+                out[i] = __fmul_rn(__fmul_rn(g, g), __uint_as_float(h[i]));
+            }
         }
     }
 }
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void *__restrict__
 // through LDS in wave order, so results are deterministic.
 //
 // AM = -1: activations arrive quantised (int8 q, fp32 s_a).
-// AM = 0/1/2 (XM of load8): fused quantisation by QW extra "quant waves"
+// AM = 0..3 (XM of load8): fused quantisation by QW extra "quant waves"
 // (waves nwc .. nwc+QW-1), token-parallel: quant wave qw handles tokens
 // qw, qw+QW, ...; it reads the token (pass 1: amax), re-reads it (pass 2:
 // quantise, same arithmetic as quant_act_kernel) and writes int8 into an LDS
@@ -793,7 +803,7 @@ void gemv_split(int K, int *nw_out, int *per_out) {
 size_t gemv_fused_lds(int M, int K, int nw) { return gemv_fused_region(M, K, nw) + (16 + 48) * sizeof(float); }
 
 // Form of the fused quantise-and-multiply launch for activation mode xm (0 bf16,
-// 1 fp32, 2 folded fp32): every compute wave quantises its own slice when the
+// 1 fp32, 2 and 3 two-half fp32): every compute wave quantises its own slice when the
 // tokens' raw chunks fit in registers, else four extra quant waves do it.
 int gemv_fused_form(int xm, int M, int K) {
     int nw, per;
@@ -897,6 +907,14 @@ bitnet_status_t bitnet_quant_act_fold(const float *y, int M, int H, int8_t *q, f
     return launched();
 }
 
+bitnet_status_t bitnet_quant_act_relu2_glu(const float *y, int M, int H, int8_t *q, float *s_a,
+                                           hipStream_t stream) {
+    if (!y || !q || !s_a || !aligned(y, 16) || !aligned(q, 16) || !aligned(s_a, 4)) return BITNET_ERR_INVALID_ARG;
+    if (M < 1 || M > 65535 * 1024 || H < 16 || H % 16) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    quant_launch<3>(y, M, H, q, s_a, stream);
+    return launched();
+}
+
 bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q, const float *s_a,
                                  float *y, int M, int N, int K, hipStream_t stream) {
     if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
@@ -927,7 +945,9 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(x, 16) || !aligned(y, 4) ||
         !aligned(q_out, 16) || !aligned(s_a_out, 4))
         return BITNET_ERR_INVALID_ARG;
-    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32 && xdt != BITNET_DT_F32_FOLD2) return BITNET_ERR_INVALID_ARG;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32 && xdt != BITNET_DT_F32_FOLD2 &&
+        xdt != BITNET_DT_F32_RELU2_GLU)
+        return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     int nw, per;
     gemv_split(K, &nw, &per);
@@ -936,7 +956,8 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
     bool ok;
     if (xdt == BITNET_DT_BF16) ok = gemv_launch<0, false>(a, stream);
     else if (xdt == BITNET_DT_F32) ok = gemv_launch<1, false>(a, stream);
-    else ok = gemv_launch<2, false>(a, stream);
+    else if (xdt == BITNET_DT_F32_FOLD2) ok = gemv_launch<2, false>(a, stream);
+    else ok = gemv_launch<3, false>(a, stream);
     if (!ok) return BITNET_ERR_UNSUPPORTED_SHAPE;
     return launched();
 }
@@ -960,7 +981,7 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
 // --------------------------------------------------------------------------
 // a7: a chain of products with per-token requantisation between them (the
 // decode pass through a stack of BitNet linear layers).  Host-side loop that
-// enqueues one fused quantise-and-multiply launch per layer (M <= 4), or a
+// enqueues one fused quantise-and-multiply launch per layer (M <= 2), or a
 // quantisation launch and a product launch; intermediate fp32 activations
 // ping-pong between two halves of the caller's workspace.
 // --------------------------------------------------------------------------
@@ -981,6 +1002,8 @@ bitnet_status_t chain_plan(const bitnet_chain_layer_t *layers, int n, int M, int
         if (!L.packed || !L.scales || !aligned(L.packed, 16) || !aligned(L.scales, 16)) return BITNET_ERR_INVALID_ARG;
         if (!shape_ok(L.N, L.K)) return BITNET_ERR_UNSUPPORTED_SHAPE;
         const int in = i == 0 ? x_width : layers[i - 1].N;
+        if (L.fold_input < BITNET_JUNCTION_NONE || L.fold_input > BITNET_JUNCTION_RELU2_GLU)
+            return BITNET_ERR_INVALID_ARG;
         if (L.fold_input ? (in != 2 * L.K) : (in != L.K)) return BITNET_ERR_UNSUPPORTED_SHAPE;
         if (i == 0 && L.fold_input) return BITNET_ERR_UNSUPPORTED_SHAPE;
         maxN = L.N > maxN ? L.N : maxN;
@@ -1021,23 +1044,28 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
     for (int i = 0; i < n; ++i) {
         const bitnet_chain_layer_t &L = layers[i];
         float *out = (i == n - 1) ? y : act[i & 1];
-        const int dt = L.fold_input ? BITNET_DT_F32_FOLD2 : in_dt;
+        const int dt = L.fold_input == BITNET_JUNCTION_SUM         ? BITNET_DT_F32_FOLD2
+                       : L.fold_input == BITNET_JUNCTION_RELU2_GLU ? BITNET_DT_F32_RELU2_GLU
+                                                                   : in_dt;
         int nw, per;
         gemv_split(L.K, &nw, &per);
         // one launch when the cheap fused form applies, else quantise + multiply
-        const bool fused = per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
-                           gemv_fused_form(dt == BITNET_DT_BF16 ? 0 : dt == BITNET_DT_F32 ? 1 : 2, M, L.K) == kAllWaves;
+        // (the fused form re-quantises in every workgroup: worth it for one or two tokens)
+        const bool fused = M <= 2 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
+                           gemv_fused_form(dt, M, L.K) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
             bool ok;
             if (dt == BITNET_DT_BF16) ok = gemv_launch<0, false>(a, stream);
             else if (dt == BITNET_DT_F32) ok = gemv_launch<1, false>(a, stream);
-            else ok = gemv_launch<2, false>(a, stream);
+            else if (dt == BITNET_DT_F32_FOLD2) ok = gemv_launch<2, false>(a, stream);
+            else ok = gemv_launch<3, false>(a, stream);
             if (!ok) return BITNET_ERR_UNSUPPORTED_SHAPE;
         } else {
             if (dt == BITNET_DT_BF16) quant_launch<0>(in, M, L.K, q, s_a, stream);
             else if (dt == BITNET_DT_F32) quant_launch<1>(in, M, L.K, q, s_a, stream);
-            else quant_launch<2>(in, M, L.K, q, s_a, stream);
+            else if (dt == BITNET_DT_F32_FOLD2) quant_launch<2>(in, M, L.K, q, s_a, stream);
+            else quant_launch<3>(in, M, L.K, q, s_a, stream);
             GemvArgs a{L.packed, L.scales, q, s_a, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
             gemv_launch<-1, false>(a, stream);
         }

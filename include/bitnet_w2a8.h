@@ -74,8 +74,18 @@ typedef enum {
 typedef enum {
     BITNET_DT_BF16 = 0,      /* bfloat16 */
     BITNET_DT_F32 = 1,       /* fp32 */
-    BITNET_DT_F32_FOLD2 = 2  /* fp32 [M][2K] read as h = x[:, :K] + x[:, K:] (one fp32 add) */
+    BITNET_DT_F32_FOLD2 = 2, /* fp32 [M][2K] read as h = x[:, :K] + x[:, K:] (one fp32 add) */
+    BITNET_DT_F32_RELU2_GLU = 3 /* fp32 [M][2K] read as h = relu(x[:, :K])^2 * x[:, K:]
+                                   (fp32: r = max(x, 0), then r * r, then times the second
+                                   half; two roundings, no fused multiply-add) */
 } bitnet_dtype_t;
+
+/* Junction between layers of a decode chain (bitnet_chain_layer_t.fold_input). */
+typedef enum {
+    BITNET_JUNCTION_NONE = 0,     /* input = previous output [M][K] */
+    BITNET_JUNCTION_SUM = 1,      /* previous output [M][2K]; input = lo + hi */
+    BITNET_JUNCTION_RELU2_GLU = 2 /* previous output [M][2K] = (gate | up); input = relu(gate)^2 * up */
+} bitnet_junction_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *bitnet_status_str(int status);
@@ -145,6 +155,17 @@ bitnet_status_t bitnet_quant_act(const void *x, int xdt, int M, int K, int8_t *q
 bitnet_status_t bitnet_quant_act_fold(const float *y, int M, int H, int8_t *q, float *s_a,
                                       hipStream_t stream);
 
+/* Squared-ReLU gated junction ([P4] "BitRun v0.2 measured" -- "Architecture-
+ * specific SIMD acceleration" pairs the ternary kernels with a squared-ReLU
+ * activation; the gated form and the half order are a reading): the fused
+ * gate+up output y [M][2H] carries the gate in columns [0, H) and the up
+ * projection in [H, 2H); h[m][j] = relu(y[m][j])^2 * y[m][H + j] in fp32 (two
+ * roundings), then quantised exactly as bitnet_quant_act does.
+ *   y    device, fp32 [M][2H];  q device int8 [M][H];  s_a device fp32 [M].
+ * Rules: M >= 1, H % 16 == 0.  Non-finite values are outside the contract. */
+bitnet_status_t bitnet_quant_act_relu2_glu(const float *y, int M, int H, int8_t *q, float *s_a,
+                                           hipStream_t stream);
+
 /* Decode product, batch 1..16 (the W2A8 GEMV of [P2] "Architecture
  * foundations", item 2), on the gfx950 int8 matrix cores.
  *   packed  device, tile layout, bitnet_packed_bytes(N,K) bytes
@@ -163,7 +184,9 @@ bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, con
  * factors, so y equals bitnet_quant_act followed by bitnet_w2a8_gemv.
  *   x        device, xdt BITNET_DT_BF16 or BITNET_DT_F32: [M][K];
  *            BITNET_DT_F32_FOLD2: fp32 [M][2K], quantised input h = x[:, :K] + x[:, K:]
- *            (the junction of a stacked decode chain, as bitnet_quant_act_fold)
+ *            (the junction of a stacked decode chain, as bitnet_quant_act_fold);
+ *            BITNET_DT_F32_RELU2_GLU: fp32 [M][2K], quantised input
+ *            h = relu(x[:, :K])^2 * x[:, K:] (as bitnet_quant_act_relu2_glu)
  *   y        device, fp32 [M][N] (out)
  *   q_out    device, int8 [M][K] (out, optional: NULL to skip)
  *   s_a_out  device, fp32 [M] (out, optional: NULL to skip)
@@ -187,8 +210,10 @@ typedef struct {
     const uint8_t *packed;  /* device, tile layout of an N x K ternary matrix */
     const float *scales;    /* device, tiled block scales */
     int N, K;
-    int fold_input;         /* 0: input is the previous output [M][K]; 1: the previous output is
-                               [M][2K] and the input is h = prev[:, :K] + prev[:, K:] */
+    int fold_input;         /* a bitnet_junction_t: 0 the input is the previous output [M][K];
+                               1 the previous output is [M][2K] and the input is
+                               h = prev[:, :K] + prev[:, K:]; 2 the input is
+                               h = relu(prev[:, :K])^2 * prev[:, K:] */
 } bitnet_chain_layer_t;
 
 /* Workspace bytes bitnet_w2a8_chain needs for these layers at batch M (0 if the
@@ -198,11 +223,14 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
 
 /* Decode pass through a stack of n W2A8 linear layers: layer i quantises its
  * input per token exactly as bitnet_quant_act (or bitnet_quant_act_fold when
- * fold_input) and multiplies as bitnet_w2a8_gemv; its fp32 output is the next
+ * fold_input 1, bitnet_quant_act_relu2_glu when 2) and multiplies as
+ * bitnet_w2a8_gemv; its fp32 output is the next
  * layer's input.  This is the chained decode of a BitNet model's linear layers
  * ([P2] "Architecture foundations": W2A8 products; [P3] "Why WASM": a 2.4B ternary
- * model), with the fused gate+up output folded to the down-projection width
- * (the plain linear reading of the junction).  One launch per layer when M <= 4.
+ * model), with the fused gate+up output brought to the down-projection width
+ * by the linear fold or the squared-ReLU gate.  One launch per layer when M <= 2
+ * (re-quantisation fused into the product), else two.
+ * A fold_input outside 0..2 gives BITNET_ERR_INVALID_ARG.
  *   layers     host array of n descriptors (device pointers inside)
  *   x          device, [M][layers[0].K], xdt BITNET_DT_BF16 or BITNET_DT_F32
  *   y          device, fp32 [M][layers[n-1].N] (out)

@@ -164,3 +164,12 @@ def test_product_path_has_no_fallback(monkeypatch):
     monkeypatch.setattr(bn, "LIB_PATH", os.path.join(ROOT, "does_not_exist.so"))
     with pytest.raises(RuntimeError):
         bn.lib()
+
+
+def test_junction_codes():
+    assert [bn.junction_code(j) for j in (False, None, "none", 0)] == [0, 0, 0, 0]
+    assert [bn.junction_code(j) for j in (True, "sum", 1)] == [1, 1, 1]
+    assert [bn.junction_code(j) for j in ("relu2_glu", 2)] == [2, 2]
+    for bad in ("relu", 3, -1, 2.5):
+        with pytest.raises(ValueError):
+            bn.junction_code(bad)

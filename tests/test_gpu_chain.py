@@ -7,6 +7,8 @@ product tolerance).  The chain equals the products called one by one, bit for
 bit.  End to end over the full 30-layer stack only statistical agreement can
 hold, because the fp32 summation order differs from the oracle's fp64 and
 requantisation turns last-bit differences into occasional +-1 steps."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -28,11 +30,12 @@ def host(t):
     return t.cpu().numpy()
 
 
-# (N, K, fold): K of a folded layer is half the previous N
+# (N, K, junction in front): K of a layer behind a junction is half the previous N
 SMALL = [(256, 512, False), (384, 256, False), (1024, 384, False), (384, 512, True), (128, 384, False)]
+JUNCTIONS = ["sum", "relu2_glu"]
 
 
-def _small_chain(seed):
+def _small_chain(seed, junction="sum"):
     Ts, Ss, ws = [], [], []
     for i, (N, K, f) in enumerate(SMALL):
         r = wl.rng_for(71, seed, i)
@@ -41,12 +44,17 @@ def _small_chain(seed):
         Ts.append(T)
         Ss.append(S)
         ws.append(bn.PackedWeight.from_ternary(T, S))
-    return Ts, Ss, ws, [f for (_, _, f) in SMALL]
+    return Ts, Ss, ws, [junction if f else False for (_, _, f) in SMALL]
 
 
+def _oracle_junction(junction, prev):
+    return oracle.fold_quant(prev) if junction == "sum" else oracle.glu_quant(prev)
+
+
+@pytest.mark.parametrize("junction", JUNCTIONS)
 @pytest.mark.parametrize("M", [1, 3, 8])
-def test_chain_layer_local_parity(gpu, M):
-    Ts, Ss, ws, folds = _small_chain(M)
+def test_chain_layer_local_parity(gpu, M, junction):
+    Ts, Ss, ws, folds = _small_chain(M, junction)
     xb = wl.normal_act(wl.rng_for(72, M), M, SMALL[0][1])
     x = dev(xb.view(np.int16)).view(torch.bfloat16)
     prev = None
@@ -55,7 +63,7 @@ def test_chain_layer_local_parity(gpu, M):
         if k == 0:
             q, s = oracle.quant_act_bf16(xb)
         elif folds[k]:
-            q, s = oracle.fold_quant(prev)
+            q, s = _oracle_junction(folds[k], prev)
         else:
             q, s = oracle.quant_act_f32(prev)
         N, K, _ = SMALL[k]
@@ -65,9 +73,10 @@ def test_chain_layer_local_parity(gpu, M):
         prev = y
 
 
+@pytest.mark.parametrize("junction", JUNCTIONS)
 @pytest.mark.parametrize("M", [1, 2, 8])
-def test_chain_equals_products_called_one_by_one(gpu, M):
-    Ts, Ss, ws, folds = _small_chain(10 + M)
+def test_chain_equals_products_called_one_by_one(gpu, M, junction):
+    Ts, Ss, ws, folds = _small_chain(10 + M, junction)
     xb = wl.normal_act(wl.rng_for(73, M), M, SMALL[0][1])
     x = dev(xb.view(np.int16)).view(torch.bfloat16)
     y_chain = host(bn.Chain(ws, folds)(x))
@@ -76,7 +85,12 @@ def test_chain_equals_products_called_one_by_one(gpu, M):
         if M <= 4:
             h = bn.bitnet_w2a8_gemv_act(w.packed, w.scales, h, w.N, w.K, fold=f)
         else:
-            q, s = bn.bitnet_quant_act_fold(h) if f else bn.bitnet_quant_act(h)
+            if f == "sum":
+                q, s = bn.bitnet_quant_act_fold(h)
+            elif f:
+                q, s = bn.bitnet_quant_act_relu2_glu(h)
+            else:
+                q, s = bn.bitnet_quant_act(h)
             h = bn.bitnet_w2a8_gemv(w.packed, w.scales, q, s, w.N, w.K)
     assert np.array_equal(y_chain.view(np.uint32), host(h).view(np.uint32))
 
@@ -90,6 +104,15 @@ def test_chain_rejects_mismatched_shapes(gpu):
         bn.Chain(ws[:4], [False, False, False, False])(x)  # the fold is missing
     with pytest.raises(bn.BitnetError):
         bn.Chain(ws[:1], [True])(x)                        # layer 0 cannot fold
+    # no such junction: the C entry point rejects it before any launch
+    good = bn.Chain(ws[:4], [False, False, False, "sum"])
+    ws_buf = good.workspace(1)
+    y = torch.empty((1, ws[3].N), dtype=torch.float32, device="cuda")
+    good._arr[3].fold_input = 3
+    st = bn.lib().bitnet_w2a8_chain(ctypes.cast(good._arr, ctypes.c_void_p), 4, x.data_ptr(), bn.BITNET_DT_BF16, 1,
+                                    y.data_ptr(), ws_buf.data_ptr(), ws_buf.numel(), None)
+    assert st == bn.BITNET_ERR_INVALID_ARG
+    assert bn.lib().bitnet_w2a8_chain_workspace_bytes(ctypes.cast(good._arr, ctypes.c_void_p), 4, 1) == 0
 
 
 def _oracle_chain(oracle_layers, folds, xb):

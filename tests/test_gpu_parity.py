@@ -110,6 +110,18 @@ def test_quant_fold_bitexact(gpu, M, H):
     assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
 
 
+@pytest.mark.parametrize("M,H", [(1, 6912), (8, 6912), (3, 48)])
+def test_quant_relu2_glu_bitexact(gpu, M, H):
+    y = wl.rng_for(53, M, H).standard_normal((M, 2 * H)).astype(np.float32) * 3
+    if M > 1:
+        y[1, :H] = -np.abs(y[1, :H])  # every gate negative -> zero token
+    q, s = bn.bitnet_quant_act_relu2_glu(dev(y))
+    qo, so = oracle.glu_quant(y)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    if M > 1:
+        assert not np.any(host(q)[1])
+
+
 # ------------------------------------------------------------------ exact integer core
 SMALL_SHAPES = [(16, 128), (48, 384), (80, 640), (272, 2688), (64, 8960), (2064, 128 * 3)]
 
@@ -174,7 +186,7 @@ def test_zero_weights_and_zero_tokens(gpu):
 
 
 # ------------------------------------------------------------------ fused quantise-and-multiply
-@pytest.mark.parametrize("mode", ["bf16", "f32", "fold"])
+@pytest.mark.parametrize("mode", ["bf16", "f32", "fold", "relu2_glu"])
 @pytest.mark.parametrize("M,N,K", [(1, 48, 384), (2, 272, 2688), (3, 80, 640), (5, 160, 6912), (8, 2064, 2560),
                                    (16, 32, 128), (1, 64, 12288)])
 def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
@@ -186,18 +198,23 @@ def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
         qd, sd = bn.bitnet_quant_act(xd)
     else:
         x = wl.bf16_to_f32(c.x_bits) * np.float32(0.37)
-        if mode == "fold":
+        if mode in ("fold", "relu2_glu"):
             x = np.concatenate([x, wl.rng_for(61, M, K).standard_normal((M, K)).astype(np.float32)], axis=1)
-            qo, so = oracle.fold_quant(x)
             xd = dev(x)
-            qd, sd = bn.bitnet_quant_act_fold(xd)
+            if mode == "fold":
+                qo, so = oracle.fold_quant(x)
+                qd, sd = bn.bitnet_quant_act_fold(xd)
+            else:
+                qo, so = oracle.glu_quant(x)
+                qd, sd = bn.bitnet_quant_act_relu2_glu(xd)
         else:
             qo, so = oracle.quant_act_f32(x)
             xd = dev(x)
             qd, sd = bn.bitnet_quant_act(xd)
     q_out = torch.empty((M, K), dtype=torch.int8, device="cuda")
     s_out = torch.empty((M,), dtype=torch.float32, device="cuda")
-    y = bn.bitnet_w2a8_gemv_act(p, st, xd, N, K, fold=(mode == "fold"), q_out=q_out, s_a_out=s_out)
+    junction = {"fold": "sum", "relu2_glu": "relu2_glu"}.get(mode, False)
+    y = bn.bitnet_w2a8_gemv_act(p, st, xd, N, K, fold=junction, q_out=q_out, s_a_out=s_out)
     y_ref = bn.bitnet_w2a8_gemv(p, st, qd, sd, N, K)
     assert np.array_equal(host(q_out), qo) and np.array_equal(host(s_out), so)
     yh = host(y)
