@@ -44,6 +44,10 @@ def _load():
             "oracle_f32_to_bf16": [p, i64, p],
             "oracle_fold_quant": [p, i64, i64, p, p, p],
             "oracle_glu_quant": [p, i64, i64, p, p, p],
+            "oracle_ternarize_absmean_g": [p, i64, i64, ctypes.c_int, p, p],
+            "oracle_pack_i2s_g": [p, i64, i64, ctypes.c_int, p],
+            "oracle_unpack_i2s_g": [p, i64, i64, ctypes.c_int, p],
+            "oracle_w2a8_g": [p, p, p, p, i64, i64, i64, ctypes.c_int, p, p, p, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -172,3 +176,53 @@ def glu_quant(y):
     scratch = np.empty((M, H), np.float32)
     _check(_load().oracle_glu_quant(_ptr(y), M, H, _ptr(q), _ptr(s), _ptr(scratch)), "glu_quant")
     return q, s
+
+
+# ---------------------------------------------------------------- scale granularity G
+# G = 128 (x86 block), 64 (ARM block) or 0 (one scale for the whole matrix).
+def scale_shape(N, K, G):
+    return (1,) if G == 0 else (N, K // G)
+
+
+def ternarize_absmean_g(W, G):
+    """fp32 [N][K] -> (T int8 [N][K], S fp32 scale_shape(N, K, G))."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), np.int8)
+    S = np.empty(scale_shape(N, K, G), np.float32)
+    _check(_load().oracle_ternarize_absmean_g(_ptr(W), N, K, G, _ptr(T), _ptr(S)), "ternarize_g")
+    return T, S
+
+
+def pack_i2s_g(T, G):
+    """Ternary int8 [N][K] -> canonical bytes uint8 [N][K/4] for granularity G."""
+    T = _c(T, np.int8)
+    N, K = T.shape
+    P = np.empty((N, K // 4), np.uint8)
+    _check(_load().oracle_pack_i2s_g(_ptr(T), N, K, G, _ptr(P)), "pack_i2s_g")
+    return P
+
+
+def unpack_i2s_g(P, K, G):
+    P = _c(P, np.uint8)
+    N = P.shape[0]
+    T = np.empty((N, K), np.int8)
+    _check(_load().oracle_unpack_i2s_g(_ptr(P), N, K, G, _ptr(T)), "unpack_i2s_g")
+    return T
+
+
+def w2a8_g(P, S, Q, s_a, N, K, G):
+    """Product with scale granularity G over canonical bytes for G; as w2a8."""
+    P = _c(P, np.uint8)
+    S = _c(S, np.float32)
+    Q = _c(Q, np.int8)
+    s_a = _c(s_a, np.float32)
+    M = Q.shape[0]
+    assert P.shape == (N, K // 4) and S.shape == scale_shape(N, K, G) and Q.shape == (M, K)
+    acc = np.empty((M, N), np.int32)
+    y64 = np.empty((M, N), np.float64)
+    y = np.empty((M, N), np.float32)
+    mag = np.empty((M, N), np.float64)
+    _check(_load().oracle_w2a8_g(_ptr(P), _ptr(S), _ptr(Q), _ptr(s_a), M, N, K, G,
+                                 _ptr(acc), _ptr(y64), _ptr(y), _ptr(mag)), "w2a8_g")
+    return {"acc": acc, "y64": y64, "y": y, "mag": mag}

@@ -291,3 +291,128 @@ int oracle_glu_quant(const float *y, int64_t M, int64_t H, int8_t *q, float *s_a
         }
     return oracle_quant_act_f32(scratch, M, H, q, s_a);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Format variants: the scale granularity G.                                  */
+/* [P3] "What i2_s actually is": blocks of 128 weights on x86 and of 64 on    */
+/* ARM, each block carrying one float scale.  G = 128 is the x86 format of    */
+/* the functions above; G = 64 is the ARM block; G = 0 is one scale for the   */
+/* whole matrix (the reading in which the scale is applied once, after the    */
+/* whole integer sum).  Readings: with G = 64 the canonical bytes of a block  */
+/* hold its 64 weights as four 16-wide groups (byte j of block b holds        */
+/* k = 64b + 16g + j, g = 0 in bits 7..6), the 128-block rule scaled down;    */
+/* with G = 0 the canonical bytes use the 128 layout, gamma is the mean |W|   */
+/* over the whole matrix (fp64 sum in row-major index order, divided by N*K,  */
+/* rounded once to fp32), and y = s_a * (S * acc) in fp64, rounded once.      */
+/* ------------------------------------------------------------------------ */
+static int64_t canon_block(int G) { return G == 64 ? 64 : 128; }
+static int gran_ok(int G) { return G == 0 || G == 64 || G == 128; }
+
+static int8_t ternary_of(float w, float gamma)
+{
+    if (gamma == 0.0f) return 0;
+    volatile float ratio = w / gamma;
+    float r = rintf(ratio);
+    if (r > 1.0f) r = 1.0f;
+    if (r < -1.0f) r = -1.0f;
+    return (int8_t)r;
+}
+
+int oracle_ternarize_absmean_g(const float *W, int64_t N, int64_t K, int G, int8_t *T, float *S)
+{
+    if (!gran_ok(G) || N <= 0 || K <= 0 || K % canon_block(G)) return -1;
+    if (G == 0) {
+        double sum = 0.0;
+        for (int64_t i = 0; i < N * K; ++i) sum += fabs((double)W[i]);
+        float gamma = (float)(sum / (double)(N * K));
+        S[0] = gamma;
+        for (int64_t i = 0; i < N * K; ++i) T[i] = ternary_of(W[i], gamma);
+        return 0;
+    }
+    int64_t B = K / G;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < B; ++b) {
+            const float *w = W + n * K + b * G;
+            double sum = 0.0;
+            for (int64_t i = 0; i < G; ++i) sum += fabs((double)w[i]);
+            float gamma = (float)(sum / (double)G);
+            S[n * B + b] = gamma;
+            for (int64_t i = 0; i < G; ++i) T[n * K + b * G + i] = ternary_of(w[i], gamma);
+        }
+    return 0;
+}
+
+int oracle_pack_i2s_g(const int8_t *T, int64_t N, int64_t K, int G, uint8_t *P)
+{
+    if (!gran_ok(G) || N <= 0 || K <= 0 || K % canon_block(G)) return -1;
+    const int64_t cb = canon_block(G), gw = cb / 4;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < K / cb; ++b)
+            for (int64_t j = 0; j < gw; ++j) {
+                unsigned byte = 0;
+                for (int g = 0; g < 4; ++g) {
+                    int t = T[n * K + b * cb + gw * g + j];
+                    if (t < -1 || t > 1) return -2;
+                    byte |= (unsigned)(t + 1) << (6 - 2 * g);
+                }
+                P[n * (K / 4) + b * gw + j] = (uint8_t)byte;
+            }
+    return 0;
+}
+
+int oracle_unpack_i2s_g(const uint8_t *P, int64_t N, int64_t K, int G, int8_t *T)
+{
+    if (!gran_ok(G) || N <= 0 || K <= 0 || K % canon_block(G)) return -1;
+    const int64_t cb = canon_block(G), gw = cb / 4;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < K / cb; ++b)
+            for (int64_t j = 0; j < gw; ++j) {
+                unsigned byte = P[n * (K / 4) + b * gw + j];
+                for (int g = 0; g < 4; ++g) {
+                    unsigned code = (byte >> (6 - 2 * g)) & 3u;
+                    if (code == 3) return -2;
+                    T[n * K + b * cb + gw * g + j] = (int8_t)((int)code - 1);
+                }
+            }
+    return 0;
+}
+
+static int i2s_weight_g(const uint8_t *P, int64_t K, int G, int64_t n, int64_t k)
+{
+    const int64_t cb = canon_block(G), gw = cb / 4;
+    int64_t b = k / cb, r = k % cb;
+    unsigned byte = P[n * (K / 4) + b * gw + r % gw];
+    return (int)((byte >> (6 - 2 * (r / gw))) & 3u) - 1;
+}
+
+/* The product with scale granularity G; scales S are [N][K/G] row-major, or  */
+/* one value when G = 0.  Outputs as oracle_w2a8.                             */
+int oracle_w2a8_g(const uint8_t *P, const float *S, const int8_t *Q, const float *s_a,
+                  int64_t M, int64_t N, int64_t K, int G,
+                  int32_t *acc, double *y64, float *y, double *mag)
+{
+    if (!gran_ok(G) || M <= 0 || N <= 0 || K <= 0 || K % canon_block(G)) return -1;
+    const int64_t blk = G == 0 ? K : G, B = K / blk;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t total = 0;
+            double sum = 0.0, msum = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                int32_t a = 0;
+                for (int64_t i = 0; i < blk; ++i) {
+                    int64_t k = b * blk + i;
+                    a += i2s_weight_g(P, K, G, n, k) * (int32_t)Q[m * K + k];
+                }
+                total += a;
+                double term = (double)(G == 0 ? S[0] : S[n * B + b]) * (double)a;
+                sum += term;
+                msum += fabs(term);
+            }
+            double yv = (double)s_a[m] * sum;
+            if (acc) acc[m * N + n] = total;
+            if (y64) y64[m * N + n] = yv;
+            if (y) y[m * N + n] = (float)yv;
+            if (mag) mag[m * N + n] = (double)s_a[m] * msum;
+        }
+    return 0;
+}

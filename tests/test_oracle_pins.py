@@ -375,3 +375,122 @@ def test_glu_quant_negative_gate_and_symmetries():
     g2[:, :64] = -np.abs(g2[:, :64])
     qz, _ = oracle.glu_quant(np.concatenate([g2, u], axis=1))
     assert not np.any(qz[:, :64])
+
+
+# --------------------------------------------------------------------------- #
+# Scale granularity G: 64 (ARM block), 128 (x86 block), 0 (one scale)
+# --------------------------------------------------------------------------- #
+def test_pack_g64_closed_forms_and_placement():
+    for t, byte in [(0, 0x55), (1, 0xAA), (-1, 0x00)]:
+        assert np.all(oracle.pack_i2s_g(np.full((2, 128), t, np.int8), 64) == byte)
+    # worked example in 16-wide groups: t[0]=+1, t[16]=-1, t[32]=0, t[48]=+1 -> byte 0 = 10 00 01 10
+    T = np.zeros((1, 128), np.int8)
+    T[0, [0, 16, 32, 48]] = [1, -1, 0, 1]
+    P = oracle.pack_i2s_g(T, 64)
+    assert P[0, 0] == 0x86 and np.all(P[0, 1:] == 0x55)
+    # a single +1 at k lands in byte 16*(k // 64) + k % 16, at shift 6 - 2 * ((k % 64) // 16)
+    for k in [0, 5, 17, 33, 63, 64, 79, 127]:
+        T = np.zeros((1, 128), np.int8)
+        T[0, k] = 1
+        P = oracle.pack_i2s_g(T, 64)
+        want = np.full(32, 0x55, np.uint8)
+        sh = 6 - 2 * ((k % 64) // 16)
+        want[16 * (k // 64) + k % 16] = (0x55 & ~(3 << sh)) | (2 << sh)
+        assert np.array_equal(P[0], want), k
+
+
+def test_pack_g64_exhaustive_roundtrip():
+    quads = np.array(np.meshgrid(*[[-1, 0, 1]] * 4, indexing="ij")).reshape(4, -1).T  # 81 x 4
+    T = np.zeros((81, 128), np.int8)
+    for r, qd in enumerate(quads):
+        for g in range(4):
+            T[r, 16 * g + 3] = qd[g]
+            T[r, 64 + 16 * g + 9] = -qd[g]
+    assert np.array_equal(oracle.unpack_i2s_g(oracle.pack_i2s_g(T, 64), 128, 64), T)
+    assert len(set(oracle.pack_i2s_g(T, 64)[:, 3].tolist())) == 81
+
+
+def test_pack_g_rejects_bad_input():
+    with pytest.raises(ValueError):
+        oracle.pack_i2s_g(np.full((1, 128), 2, np.int8), 64)
+    with pytest.raises(ValueError):
+        oracle.pack_i2s_g(np.zeros((1, 128), np.int8), 32)
+    with pytest.raises(ValueError):
+        oracle.unpack_i2s_g(np.full((1, 32), 0xFF, np.uint8), 128, 64)
+
+
+@pytest.mark.parametrize("G", [0, 64])
+def test_ternarize_g_recovers_scaled_ternary(G):
+    rng = np.random.default_rng(43 + G)
+    N, K = 4, 256  # N*K = 1024, a power of two: the per-matrix mean is exact
+    T = (rng.integers(0, 3, size=(N, K)) - 1).astype(np.int8)
+    T[:, ::32] = 1  # every block has a nonzero
+    c = np.float32(0.75)
+    T2, S = oracle.ternarize_absmean_g(T.astype(np.float32) * c, G)
+    assert np.array_equal(T2, T)
+    if G == 0:
+        assert S.shape == (1,) and S[0] == np.float32(0.75 * np.count_nonzero(T) / (N * K))
+    else:
+        nnz = np.count_nonzero(T.reshape(N, K // 64, 64), axis=2)
+        assert np.array_equal(S, (0.75 * nnz / 64).astype(np.float32))
+    Tn, Sn = oracle.ternarize_absmean_g(-T.astype(np.float32) * c, G)
+    assert np.array_equal(Tn, -T) and np.array_equal(Sn, S)
+
+
+@pytest.mark.parametrize("G", [0, 64])
+def test_ternarize_g_gaussian_zero_fraction(G):
+    W = wl.rng_for(44, G).normal(0, 0.02, size=(256, 1024)).astype(np.float32)
+    T, S = oracle.ternarize_absmean_g(W, G)
+    # as for 128-blocks: P(|Z| < sqrt(2/pi)/2) = 0.3101; shorter blocks add a little spread
+    assert abs(float((T == 0).mean()) - 0.3101) < 0.012
+
+
+@pytest.mark.parametrize("G", [0, 64])
+@pytest.mark.parametrize("M,N,K,seed", [(1, 16, 128, 1), (3, 32, 256, 2), (8, 64, 384, 3)])
+def test_w2a8_g_brute_force_and_unit_scales(G, M, N, K, seed):
+    r = wl.rng_for(45, G, seed)
+    T = (r.integers(0, 3, size=(N, K)) - 1).astype(np.int8)
+    Q = r.integers(-127, 128, size=(M, K)).astype(np.int8)
+    P = oracle.pack_i2s_g(T, G)
+    ones = np.ones(oracle.scale_shape(N, K, G), np.float32)
+    out = oracle.w2a8_g(P, ones, Q, np.ones(M, np.float32), N, K, G)
+    brute = Q.astype(np.int64) @ T.astype(np.int64).T
+    assert np.array_equal(out["acc"], brute)
+    assert np.array_equal(out["y"], brute.astype(np.float32))  # |acc| < 2^24: exact
+
+
+def test_w2a8_g64_uses_each_half_scale():
+    # +1 weights only in one 64-half of a 128-block, unit activations: y = s_a * S[half] * 64
+    N, K = 16, 256
+    S = wl.rng_for(46).uniform(0.5, 2, size=(N, K // 64)).astype(np.float32)
+    Q = np.ones((1, K), np.int8)
+    s_a = np.array([0.5], np.float32)
+    for half in range(4):
+        T = np.zeros((N, K), np.int8)
+        T[:, 64 * half:64 * half + 64] = 1
+        out = oracle.w2a8_g(oracle.pack_i2s_g(T, 64), S, Q, s_a, N, K, 64)
+        assert np.array_equal(out["acc"][0], np.full(N, 64))
+        assert np.array_equal(out["y64"][0], 0.5 * S[:, half].astype(np.float64) * 64)
+
+
+def test_w2a8_g_reduces_to_block128():
+    # exact reductions to the pinned 128-block product (scales from {0.5, 1, 1.5, 2}:
+    # every partial sum is exact in fp64, so the results agree bit for bit)
+    r = wl.rng_for(47)
+    M, N, K = 4, 48, 384
+    T = (r.integers(0, 3, size=(N, K)) - 1).astype(np.int8)
+    Q = r.integers(-127, 128, size=(M, K)).astype(np.int8)
+    s_a = r.uniform(0.01, 0.1, size=M).astype(np.float32)
+    S128 = (r.integers(1, 5, size=(N, K // 128)) * 0.5).astype(np.float32)
+    ref = oracle.w2a8(oracle.pack_i2s(T), S128, Q, s_a, N, K)
+    out64 = oracle.w2a8_g(oracle.pack_i2s_g(T, 64), np.repeat(S128, 2, axis=1), Q, s_a, N, K, 64)
+    assert np.array_equal(out64["y64"], ref["y64"]) and np.array_equal(out64["acc"], ref["acc"])
+    c = np.float32(1.5)
+    ref_c = oracle.w2a8(oracle.pack_i2s(T), np.full((N, K // 128), c, np.float32), Q, s_a, N, K)
+    out0 = oracle.w2a8_g(oracle.pack_i2s_g(T, 0), np.array([c]), Q, s_a, N, K, 0)
+    assert np.array_equal(out0["y64"], ref_c["y64"]) and np.array_equal(out0["y"], ref_c["y"])
+    # sign flip negates; doubling the one scale doubles y exactly
+    neg = oracle.w2a8_g(oracle.pack_i2s_g(-T, 0), np.array([c]), Q, s_a, N, K, 0)
+    assert np.array_equal(neg["y64"], -out0["y64"])
+    dbl = oracle.w2a8_g(oracle.pack_i2s_g(T, 0), np.array([2 * c]), Q, s_a, N, K, 0)
+    assert np.array_equal(dbl["y64"], 2 * out0["y64"])
