@@ -65,6 +65,17 @@ _SIGS = {
                                     ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemv": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemm": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_scale_count_g": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int], ctypes.c_size_t),
+    "bitnet_ternarize_absmean_g": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p], ctypes.c_int),
+    "bitnet_pack_i2s_g": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                           ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_repack_i2s_g": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                             ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_unpack_i2s_g": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                             ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemv_g": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemm_g": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemv_act": ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3
                              + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_acc_i32": ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
@@ -195,6 +206,70 @@ def bitnet_unpack_i2s(packed: np.ndarray, scales_tiled: np.ndarray | None, N: in
     return t, s
 
 
+# ------------------------------------------------------------------ scale granularity
+# scale_block: 128 (x86 i2_s blocks, the default everywhere else), 64 (ARM
+# blocks) or 0 (one scale for the whole matrix).
+def scale_shape(N: int, K: int, scale_block: int):
+    return (1,) if scale_block == 0 else (N, K // scale_block)
+
+
+def bitnet_scale_count_g(N: int, K: int, scale_block: int) -> int:
+    return lib().bitnet_scale_count_g(N, K, scale_block)
+
+
+def bitnet_ternarize_absmean_g(w: np.ndarray, scale_block: int):
+    """fp32 [N][K] -> (ternary int8 [N][K], scales fp32 scale_shape(N, K, scale_block))."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    t = np.empty((N, K), np.int8)
+    s = np.empty(scale_shape(N, K, scale_block), np.float32)
+    _ok(lib().bitnet_ternarize_absmean_g(_np_ptr(w), N, K, scale_block, _np_ptr(t), _np_ptr(s)),
+        "bitnet_ternarize_absmean_g")
+    return t, s
+
+
+def _pack_g(name, src, scales, N, K, scale_block):
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    if scales.shape != scale_shape(N, K, scale_block):
+        raise ValueError("scales must have shape %s" % (scale_shape(N, K, scale_block),))
+    nb, ns = bitnet_packed_bytes(N, K), bitnet_scale_count_g(N, K, scale_block)
+    if nb == 0 or ns == 0:
+        raise BitnetError(BITNET_ERR_UNSUPPORTED_SHAPE, name)
+    packed = np.empty(nb, np.uint8)
+    st = np.empty(ns, np.float32)
+    _ok(getattr(lib(), name)(_np_ptr(src), _np_ptr(scales), N, K, scale_block, _np_ptr(packed), _np_ptr(st)), name)
+    return packed, st
+
+
+def bitnet_pack_i2s_g(ternary: np.ndarray, scales: np.ndarray, scale_block: int):
+    """As bitnet_pack_i2s, scales of shape scale_shape(N, K, scale_block)."""
+    ternary = np.ascontiguousarray(ternary, dtype=np.int8)
+    N, K = ternary.shape
+    return _pack_g("bitnet_pack_i2s_g", ternary, scales, N, K, scale_block)
+
+
+def bitnet_repack_i2s_g(i2s: np.ndarray, scales: np.ndarray, K: int, scale_block: int):
+    """Canonical bytes of the given format uint8 [N][K/4] + scales -> (packed, tiled scales)."""
+    i2s = np.ascontiguousarray(i2s, dtype=np.uint8)
+    N = i2s.shape[0]
+    if i2s.shape != (N, K // 4):
+        raise ValueError("bad i2s shape")
+    return _pack_g("bitnet_repack_i2s_g", i2s, scales, N, K, scale_block)
+
+
+def bitnet_unpack_i2s_g(packed: np.ndarray, scales_tiled, N: int, K: int, scale_block: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    t = np.empty((N, K), np.int8)
+    s = sp = None
+    if scales_tiled is not None:
+        scales_tiled = np.ascontiguousarray(scales_tiled, dtype=np.float32)
+        s = np.empty(scale_shape(N, K, scale_block), np.float32)
+        sp = _np_ptr(scales_tiled)
+    _ok(lib().bitnet_unpack_i2s_g(_np_ptr(packed), sp, N, K, scale_block, _np_ptr(t),
+                                  None if s is None else _np_ptr(s)), "bitnet_unpack_i2s_g")
+    return t, s
+
+
 # ------------------------------------------------------------------ device, async
 def bitnet_quant_act(x, q=None, s_a=None, stream=None):
     """x: device [M][K] bf16 or fp32 -> (q int8 [M][K], s_a fp32 [M])."""
@@ -288,6 +363,36 @@ def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=N
     _ok(lib().bitnet_w2a8_gemm(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), ydt, M, N, K, _stream(stream)),
         "bitnet_w2a8_gemm")
+    return y
+
+
+def bitnet_w2a8_gemv_g(packed, scales, q, s_a, N: int, K: int, scale_block: int, y=None, stream=None):
+    """Decode product at scale granularity scale_block (tiled scales of bitnet_pack_i2s_g)."""
+    import torch
+    M = q.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    _ok(lib().bitnet_w2a8_gemv_g(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
+                                 _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), M, N, K, scale_block, _stream(stream)),
+        "bitnet_w2a8_gemv_g")
+    return y
+
+
+def bitnet_w2a8_gemm_g(packed, scales, q, s_a, N: int, K: int, scale_block: int, out_dtype=None, y=None,
+                       stream=None):
+    """Prefill product at scale granularity scale_block."""
+    import torch
+    M = q.shape[0]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if y is None else y.dtype
+    ydt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(out_dtype)
+    if ydt is None:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    _ok(lib().bitnet_w2a8_gemm_g(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
+                                 _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), ydt, M, N, K, scale_block,
+                                 _stream(stream)), "bitnet_w2a8_gemm_g")
     return y
 
 

@@ -30,6 +30,7 @@ using namespace bitnet_layout;
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kGemvMaxM = 16;
@@ -323,9 +324,10 @@ enum GemvForm {
     kQuantWaves = 4 // fused quantisation by 4 extra quant waves (4 < M <= 16)
 };
 
-template <int AM, int NB, int TOK, bool INT_OUT, int FORM>
+template <int AM, int NB, int TOK, bool INT_OUT, int FORM, int SG>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     constexpr int MW = TOK < 4 ? TOK : 4;  // accumulator elements drained per lane
+    constexpr bool IACC = INT_OUT || SG == 0;  // integer sums over the wave's whole K-slice
     extern __shared__ __align__(16) unsigned char smem[];
     const int M = args.M, N = args.N, K = args.K, per = args.per, nwc = args.nwc;
     const int nblk = K >> 7;
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) sa_pre[e] = args.s_a[min(4 * g + e, M - 1)];
     }
+    const float s_w = (SG == 0 && !INT_OUT) ? args.scales[0] : 0.0f;  // the one weight scale
     // kAllWaves: this wave's K-slice of every token, raw, 8 values per chunk
     constexpr int CR = (NB + 3) / 4;
     Raw8<XM> xr[FORM == kAllWaves ? MW : 1][FORM == kAllWaves ? CR : 1];
@@ -400,14 +403,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     auto chunk = [&](const int c0) {
         const int nb = min(NB, bw1 - c0);
         const uint8_t *wp = args.packed + ((size_t)tile * nblk + c0) * kBrickBytes + l * 8;
-        const float *sp = args.scales + ((size_t)tile * nblk + c0) * kTileN + j;
+        // scales: SG 128 [tile][block][16 rows]; SG 64 [tile][block][16 rows][2 halves]
+        const float *sp = args.scales + (((size_t)tile * nblk + c0) * kTileN + j) * (SG == 64 ? 2 : 1);
         uint2 wv[NB];
-        float sc[NB];
+        float2 sc[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {  // unconditional (clamped) loads, issued back to back
             const int bi = min(i, nb - 1);
             wv[i] = *reinterpret_cast<const uint2 *>(wp + bi * kBrickBytes);
-            if (!INT_OUT) sc[i] = sp[bi * kTileN];
+            if (!INT_OUT && SG == 128) sc[i].x = sp[bi * kTileN];
+            if (!INT_OUT && SG == 64) sc[i] = *reinterpret_cast<const float2 *>(sp + bi * 2 * kTileN);
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (FORM == kStaged) {
@@ -483,15 +488,24 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i < nb) {
-                v4i c = v4i{0, 0, 0, 0};
-                c = mfma_i8(a[i][0], decode16(wv[i].x), c);
-                c = mfma_i8(a[i][1], decode16(wv[i].y), c);
-                if (INT_OUT) {
+                if constexpr (SG == 64 && !INT_OUT) {  // one scale per matrix-core step (64 weights)
+                    const v4i c0 = mfma_i8(a[i][0], decode16(wv[i].x), v4i{0, 0, 0, 0});
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) iacc[e] += c[e];
+                    for (int e = 0; e < MW; ++e) yacc[e] = fmaf(sc[i].x, (float)c0[e], yacc[e]);
+                    const v4i c1 = mfma_i8(a[i][1], decode16(wv[i].y), v4i{0, 0, 0, 0});
+#pragma unroll
+                    for (int e = 0; e < MW; ++e) yacc[e] = fmaf(sc[i].y, (float)c1[e], yacc[e]);
                 } else {
+                    v4i c = v4i{0, 0, 0, 0};
+                    c = mfma_i8(a[i][0], decode16(wv[i].x), c);
+                    c = mfma_i8(a[i][1], decode16(wv[i].y), c);
+                    if (IACC) {
 #pragma unroll
-                    for (int e = 0; e < MW; ++e) yacc[e] = fmaf(sc[i], (float)c[e], yacc[e]);
+                        for (int e = 0; e < NE; ++e) iacc[e] += c[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < MW; ++e) yacc[e] = fmaf(sc[i].x, (float)c[e], yacc[e]);
+                    }
                 }
             }
         }
@@ -506,7 +520,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 
     if (LDSQ) lds_barrier();  // the reduction buffer overlaps the LDS copy of q
 #pragma unroll
-    for (int e = 0; e < NE; ++e) red[(w * 4 + e) * kWave + l] = INT_OUT ? iacc[e] : __float_as_int(yacc[e]);
+    for (int e = 0; e < NE; ++e) red[(w * 4 + e) * kWave + l] = IACC ? iacc[e] : __float_as_int(yacc[e]);
     if (LDSQ) lds_barrier();
     else __syncthreads();
     if (w == 0) {
@@ -518,6 +532,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
                 int sum = 0;
                 for (int ww = 0; ww < nwc; ++ww) sum += red[(ww * 4 + e) * kWave + l];
                 if (m < M) args.acc[(size_t)m * N + n] = sum >> 6;  // exact: sum is 64 * integer
+            } else if (SG == 0) {  // exact integer product, then the two scales
+                int sum = 0;
+                for (int ww = 0; ww < nwc; ++ww) sum += red[(ww * 4 + e) * kWave + l];
+                if (m < M) {
+                    const float sa = FUSED ? tail[m] : sa_pre[e];
+                    args.y[(size_t)m * N + n] = (float)(sum >> 6) * (sa * s_w);
+                }
             } else {
                 float sum = 0.0f;
                 for (int ww = 0; ww < nwc; ++ww) sum += __int_as_float(red[(ww * 4 + e) * kWave + l]);
@@ -548,8 +569,7 @@ constexpr int kGemmBM = 128, kGemmBN = 256, kGemmThreads = 512;
 constexpr int kAStride = 144;                        // padded LDS row of the activation tile
 constexpr int kAStage = kGemmBM * kAStride;          // 18432 bytes
 constexpr int kBStage = (kGemmBN / 16) * 512;        // 8192 bytes: 16 bricks
-constexpr int kSStage = kGemmBN * 4;                 // 1024 bytes: [row j][16 tiles] fp32
-constexpr int kStage = kAStage + kBStage + kSStage;  // 27648 bytes
+constexpr int kSStage = kGemmBN * 4;                 // 1024 bytes: [16 tiles][16 rows] fp32 (x2 for 64-blocks)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -557,13 +577,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-template <int OUT>  // 0: bf16 y, 1: fp32 y, 2: int32 acc
+// OUT: 0 bf16 y, 1 fp32 y, 2 int32 acc.  SG: scale granularity, 128 or 64
+// weights per scale (scales staged per block: [tile][16 rows] or
+// [tile][16 rows][2 halves]) or 0 (one scale: integer sums over all of K,
+// scaled once in the epilogue).
+template <int OUT, int SG>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                              const float *__restrict__ scales,
                                                              const int8_t *__restrict__ q,
                                                              const float *__restrict__ s_a, void *__restrict__ yout,
                                                              int M, int N, int K, int ntm) {
-    __shared__ __align__(16) unsigned char lds[2 * kStage];
+    constexpr bool BLOCKED = OUT != 2 && SG != 0;     // per-block fp32 drain with block scales
+    constexpr int SPT = SG == 64 ? 2 : 1;             // scales per row and 128-block
+    constexpr int SST = BLOCKED ? kSStage * SPT : 0;  // staged scale bytes per block
+    constexpr int STAGE = kAStage + kBStage + SST;
+    __shared__ __align__(16) unsigned char lds[2 * STAGE];
     const int G = gridDim.x;
     int t = blockIdx.x;
     if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // XCD-aware order
@@ -591,115 +619,175 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     const int bT = T0 + (tid >> 5);
     const bool bok = bT < ntile_n;
     const uint8_t *bptr = packed + (size_t)(bok ? bT : 0) * nblk * kBrickBytes + (tid & 31) * 16;
-    const int sT = T0 + (tid >> 2);
-    const bool sok = OUT != 2 && tid < 64 && sT < ntile_n;
-    const float *sptr = scales + (size_t)(sok ? sT : 0) * nblk * kTileN + (tid & 3) * 4;
+    // scale staging: 64 (SG 128) or 128 (SG 64) threads, one float4 each per block
+    constexpr int SCT = 4 * SPT;  // staging threads per tile
+    // threads past the 16 tiles' scales repeat the last tile's (not stored)
+    const int sT = T0 + min(tid / SCT, 15);
+    const bool sok = BLOCKED && sT < ntile_n;
+    const float *sptr = scales + (size_t)(sok ? sT : 0) * nblk * kTileN * SPT + (tid % SCT) * 4;
 
     // Two register sets of staged data: the loads of block b+2 are issued while
     // block b computes and block b+1's data (issued one iteration earlier) is
     // stored to LDS after it, so each block's load latency is covered by a
     // full iteration plus a barrier.
-    struct Staged {
-        uint4 a[2];
-        uint4 b;
-        float4 s;
+    struct Staged {  // native vectors: register values, not aggregates
+        v4i a[2];
+        v4i b;
+        v4f s;
     };
+    // Unconditional loads from clamped addresses (rows past M or N read row 0 /
+    // tile 0, whose products land in outputs that are never stored): branch-free
+    // issue lets the wait counters track each block's loads exactly, so the
+    // store of block b+1 does not wait for the prefetch of block b+2.
     auto gload = [&](int b, Staged &r) {
+        b = min(b, nblk - 1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            r.a[i] = aok[i] ? *reinterpret_cast<const uint4 *>(aptr[i] + (size_t)b * kBlockK) : make_uint4(0, 0, 0, 0);
-        r.b = bok ? *reinterpret_cast<const uint4 *>(bptr + (size_t)b * kBrickBytes) : make_uint4(0, 0, 0, 0);
-        r.s = sok ? *reinterpret_cast<const float4 *>(sptr + (size_t)b * kTileN) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < 2; ++i) r.a[i] = *reinterpret_cast<const v4i *>(aptr[i] + (size_t)b * kBlockK);
+        r.b = *reinterpret_cast<const v4i *>(bptr + (size_t)b * kBrickBytes);
+        if (BLOCKED) r.s = *reinterpret_cast<const v4f *>(sptr + (size_t)b * kTileN * SPT);
     };
     auto lstore = [&](int st, const Staged &r) {
-        unsigned char *base = lds + st * kStage;
+        unsigned char *base = lds + st * STAGE;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(base + arow[i] * kAStride + acol[i]) = r.a[i];
-        *reinterpret_cast<uint4 *>(base + kAStage + tid * 16) = r.b;
-        if (OUT != 2 && tid < 64)  // [tile][16 rows], the global order of one block's scales
-            *reinterpret_cast<float4 *>(base + kAStage + kBStage + tid * 16) = r.s;
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(base + arow[i] * kAStride + acol[i]) = r.a[i];
+        *reinterpret_cast<v4i *>(base + kAStage + tid * 16) = r.b;
+        // LDS scales: [half][16 tiles][16 rows]; global SG 64 order is [tile][row][half]
+        if (BLOCKED && tid < 16 * SCT) {
+            float *sb = reinterpret_cast<float *>(base + kAStage + kBStage);
+            if constexpr (SG == 128) {
+                *reinterpret_cast<v4f *>(sb + 4 * tid) = r.s;
+            } else {  // r.s = rows 2i, 2i+1 of tile tid/8, each (half 0, half 1)
+                const int tile = tid >> 3, i = tid & 7;
+                *reinterpret_cast<float2 *>(sb + tile * 16 + 2 * i) = make_float2(r.s.x, r.s.z);
+                *reinterpret_cast<float2 *>(sb + 256 + tile * 16 + 2 * i) = make_float2(r.s.y, r.s.w);
+            }
+        }
     };
 
     float yacc[4][4][4];
-    int iacc[4][4][4];
+    v4i iacc[4][4];  // unscaled paths: the matrix core accumulates over all of K
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) {
+            iacc[a][b] = v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                yacc[a][b][e] = 0.0f;
-                iacc[a][b][e] = 0;
-            }
+            for (int e = 0; e < 4; ++e) yacc[a][b][e] = 0.0f;
+        }
 
-    auto compute = [&](int st) {
-        const unsigned char *base = lds + st * kStage;
-        v4i ao[4][2];
+    // Operands of one block: activation fragments of the wave's 4 token tiles and
+    // the decoded weights of its 4 row tiles (matrix-core A = weights (rows),
+    // B = activations (tokens): lane (g, j) receives rows 4g..4g+3 of token j).
+    auto operands = [&](int st, v4i (&ao)[4][2], v4i (&bw)[4][2]) {
+        const unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 ao[ti][s] = *reinterpret_cast<const v4i *>(base + (64 * wm + 16 * ti + j) * kAStride + 64 * s + 16 * g);
-        v4i bw[4][2];
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + (4 * wn + tj) * 512 + l * 8);
             bw[tj][0] = decode16(wv.x);
             bw[tj][1] = decode16(wv.y);
         }
-        // matrix-core A = decoded weights (rows), B = activations (tokens): lane (g, j)
-        // receives rows 4g..4g+3 of token j, so the drain needs those 4 rows' scales
-        float sc[4][4];
+    };
+    // scales of rows 4g..4g+3 of the wave's 4 row tiles, for half h
+    auto load_sc = [&](int st, int h, float (&sc)[4][4]) {
+        const unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            if (OUT != 2) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(base + kAStage + kBStage +
-                                                                    ((4 * wn + tj) * 16 + 4 * g) * 4);
-                sc[tj][0] = s4.x;
-                sc[tj][1] = s4.y;
-                sc[tj][2] = s4.z;
-                sc[tj][3] = s4.w;
-            } else {
-                sc[tj][0] = sc[tj][1] = sc[tj][2] = sc[tj][3] = 0.0f;
-            }
+            const float4 s4 = *reinterpret_cast<const float4 *>(base + kAStage + kBStage + h * 1024 +
+                                                                ((4 * wn + tj) * 16 + 4 * g) * 4);
+            sc[tj][0] = s4.x;
+            sc[tj][1] = s4.y;
+            sc[tj][2] = s4.z;
+            sc[tj][3] = s4.w;
         }
-        // the 16 tiles' first K-steps are independent and pipeline on the matrix
-        // core; the second K-steps then find their accumulators long finished
-        v4i c[4][4];
+    };
+    // the 16 tiles' first K-steps are independent and pipeline on the matrix
+    // core; the second K-steps then find their accumulators long finished
+    auto mma = [&](const v4i (&ao)[4][2], const v4i (&bw)[4][2], v4i (&c)[4][4], bool from_zero) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) c[ti][tj] = mfma_i8(bw[tj][0], ao[ti][0], v4i{0, 0, 0, 0});
+            for (int tj = 0; tj < 4; ++tj)
+                c[ti][tj] = mfma_i8(bw[tj][0], ao[ti][0], from_zero ? v4i{0, 0, 0, 0} : c[ti][tj]);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) c[ti][tj] = mfma_i8(bw[tj][1], ao[ti][1], c[ti][tj]);
+    };
+    auto drain = [&](const v4i (&c)[4][4], const float (&sc)[4][4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (OUT == 2) iacc[ti][tj][e] += c[ti][tj][e];
-                    else yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
-                }
+                for (int e = 0; e < 4; ++e) yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
+    };
+
+    // Waves w and w + 4 share a SIMD.  With a barrier per block both would run
+    // their VALU phases (decode, drain) and their matrix-core phases at the same
+    // time; the upper four waves therefore drain each block one iteration late
+    // (accumulators and scales held in registers across the barrier), so that
+    // one wave's drain overlaps its partner's matrix-core steps.
+    const bool lag = w >= 4;
+    v4i cl[4][4];
+    float scl[4][4];
+
+    auto compute = [&](int st, bool first) {
+        v4i ao[4][2], bw[4][2];
+        if constexpr (SG == 64 && BLOCKED) {
+            // one scale per matrix-core step (64 weights): each half's 16 steps are
+            // drained with that half's scales, in the registers of the 128 path
+            operands(st, ao, bw);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                load_sc(st, h, scl);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int tj = 0; tj < 4; ++tj) cl[ti][tj] = mfma_i8(bw[tj][h], ao[ti][h], v4i{0, 0, 0, 0});
+                drain(cl, scl);
+                __builtin_amdgcn_sched_barrier(0);  // one set of accumulators live
+            }
+        } else if constexpr (!BLOCKED) {  // integer sums over all of K
+            operands(st, ao, bw);
+            mma(ao, bw, iacc, false);
+        } else {  // both orders use the same accumulator and scale registers
+            if (lag && !first) drain(cl, scl);  // the previous block, then start this one
+            operands(st, ao, bw);
+            load_sc(st, 0, scl);
+            mma(ao, bw, cl, true);
+            if (!lag) drain(cl, scl);
+        }
     };
 
     Staged r0, r1;
     gload(0, r0);
-    if (nblk > 1) gload(1, r1);
+    gload(1, r1);
     lstore(0, r0);
     __syncthreads();
-    // iteration b: ring slot (b & 1) is free, slot ((b + 1) & 1) holds block b+1
-    auto iter = [&](int b, Staged &freed, Staged &next) {
-        if (b + 2 < nblk) gload(b + 2, freed);
-        compute(b & 1);
-        if (b + 1 < nblk) lstore((b + 1) & 1, next);
-        __syncthreads();
-    };
+    // Block b computes from LDS slot b & 1 while block b+1 (in registers since
+    // the previous step) goes to the other slot and block b+2 is fetched into
+    // the registers just freed.  Loads past the last block repeat it and their
+    // LDS copy goes to a slot nobody reads again.  Both halves of the loop are
+    // written out with fixed register sets (no pointer selects between them).
     for (int b = 0; b < nblk; b += 2) {
-        iter(b, r0, r1);
-        if (b + 1 < nblk) iter(b + 1, r1, r0);
+        gload(b + 2, r0);
+        compute(0, b == 0);
+        lstore(1, r1);
+        lds_barrier();
+        if (b + 1 < nblk) {
+            gload(b + 3, r1);
+            compute(1, false);
+            lstore(0, r0);
+            lds_barrier();
+        }
+    }
+    if constexpr (SG != 64 && BLOCKED) {
+        if (lag) drain(cl, scl);  // the last block of the lagging waves
     }
 
     // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j,
@@ -708,19 +796,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     for (int ti = 0; ti < 4; ++ti) {
         const int m = m0 + 64 * wm + 16 * ti + j;
         if (m >= M) continue;
-        const float f = (OUT == 2) ? 0.0f : s_a[m] * 0.015625f;
+        // blocked: y = s_a * sum * 2^-6 (decoded weights are 64 t); SG 0: exact integer
+        // sum times s_a * s_w
+        const float f = (OUT == 2) ? 0.0f : BLOCKED ? s_a[m] * 0.015625f : s_a[m] * scales[0];
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             const int T = T0 + 4 * wn + tj;
             if (T >= ntile_n) continue;
             const size_t idx = (size_t)m * N + (size_t)T * 16 + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = BLOCKED ? yacc[ti][tj][e] : (float)(iacc[ti][tj][e] >> 6);
             if (OUT == 0) {
-                const uint32_t lo = f32_to_bf16_rne(yacc[ti][tj][0] * f) | ((uint32_t)f32_to_bf16_rne(yacc[ti][tj][1] * f) << 16);
-                const uint32_t hi = f32_to_bf16_rne(yacc[ti][tj][2] * f) | ((uint32_t)f32_to_bf16_rne(yacc[ti][tj][3] * f) << 16);
+                const uint32_t lo = f32_to_bf16_rne(v[0] * f) | ((uint32_t)f32_to_bf16_rne(v[1] * f) << 16);
+                const uint32_t hi = f32_to_bf16_rne(v[2] * f) | ((uint32_t)f32_to_bf16_rne(v[3] * f) << 16);
                 *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(yout) + idx) = make_uint2(lo, hi);
             } else if (OUT == 1) {
                 *reinterpret_cast<float4 *>(static_cast<float *>(yout) + idx) =
-                    make_float4(yacc[ti][tj][0] * f, yacc[ti][tj][1] * f, yacc[ti][tj][2] * f, yacc[ti][tj][3] * f);
+                    make_float4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
             } else {
                 *reinterpret_cast<int4 *>(static_cast<int32_t *>(yout) + idx) =
                     make_int4(iacc[ti][tj][0] >> 6, iacc[ti][tj][1] >> 6, iacc[ti][tj][2] >> 6, iacc[ti][tj][3] >> 6);
@@ -745,34 +838,37 @@ __host__ __device__ constexpr bool allwaves_fits(int xm, int tok, int nb) {
     return tok * ((nb + 3) / 4) * (xm == 0 ? 4 : xm == 1 ? 8 : 16) <= 64;
 }
 
-template <int AM, int NB, bool INT_OUT, int FORM>
+// SG: scale granularity (128 or 64 weights per scale, 0 = one scale for the
+// matrix); the fused forms exist for SG 128 only.
+template <int AM, int NB, bool INT_OUT, int FORM, int SG>
 void gemv_launch_tok(int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
     if constexpr (FORM == kAllWaves) {  // M <= 4 and allwaves_fits (checked by the caller)
-        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, false, FORM>), grid, block, lds, st, a);
-        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, false, FORM>), grid, block, lds, st, a);
+        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, false, FORM, 128>), grid, block, lds, st, a);
+        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, false, FORM, 128>), grid, block, lds, st, a);
         else if constexpr (allwaves_fits(AM < 0 ? 0 : AM, 4, NB))
-            hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, false, FORM>), grid, block, lds, st, a);
+            hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, false, FORM, 128>), grid, block, lds, st, a);
     } else if constexpr (FORM == kStaged) {
-        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, INT_OUT, FORM>), grid, block, lds, st, a);
-        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, INT_OUT, FORM>), grid, block, lds, st, a);
-        else if (tok == 4) hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, INT_OUT, FORM>), grid, block, lds, st, a);
-        else if (tok == 8) hipLaunchKernelGGL((gemv_kernel<AM, NB, 8, INT_OUT, FORM>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, INT_OUT, FORM>), grid, block, lds, st, a);
-    } else {  // kDirect, kMulti, kQuantWaves: token capacity 16
-        hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, (FORM == kQuantWaves ? false : INT_OUT), FORM>), grid, block, lds,
-                           st, a);
+        if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, INT_OUT, FORM, SG>), grid, block, lds, st, a);
+        else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, INT_OUT, FORM, SG>), grid, block, lds, st, a);
+        else if (tok == 4) hipLaunchKernelGGL((gemv_kernel<AM, NB, 4, INT_OUT, FORM, SG>), grid, block, lds, st, a);
+        else if (tok == 8) hipLaunchKernelGGL((gemv_kernel<AM, NB, 8, INT_OUT, FORM, SG>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, INT_OUT, FORM, SG>), grid, block, lds, st, a);
+    } else if constexpr (FORM == kQuantWaves) {
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, false, FORM, 128>), grid, block, lds, st, a);
+    } else {  // kDirect, kMulti: token capacity 16
+        hipLaunchKernelGGL((gemv_kernel<AM, NB, 16, INT_OUT, FORM, SG>), grid, block, lds, st, a);
     }
 }
 
-template <int AM, int NB, bool INT_OUT>
+template <int AM, int NB, bool INT_OUT, int SG>
 void gemv_launch_form(int form, int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
     if constexpr (AM >= 0) {
-        if (form == kQuantWaves) gemv_launch_tok<AM, NB, false, kQuantWaves>(tok, grid, block, lds, st, a);
-        else gemv_launch_tok<AM, NB, false, kAllWaves>(tok, grid, block, lds, st, a);
+        if (form == kQuantWaves) gemv_launch_tok<AM, NB, false, kQuantWaves, 128>(tok, grid, block, lds, st, a);
+        else gemv_launch_tok<AM, NB, false, kAllWaves, 128>(tok, grid, block, lds, st, a);
     } else {
-        if (form == kStaged) gemv_launch_tok<AM, NB, INT_OUT, kStaged>(tok, grid, block, lds, st, a);
-        else if (NB == 8 && form == kMulti) gemv_launch_tok<AM, 8, INT_OUT, kMulti>(tok, grid, block, lds, st, a);
-        else gemv_launch_tok<AM, NB, INT_OUT, kDirect>(tok, grid, block, lds, st, a);
+        if (form == kStaged) gemv_launch_tok<AM, NB, INT_OUT, kStaged, SG>(tok, grid, block, lds, st, a);
+        else if (NB == 8 && form == kMulti) gemv_launch_tok<AM, 8, INT_OUT, kMulti, SG>(tok, grid, block, lds, st, a);
+        else gemv_launch_tok<AM, NB, INT_OUT, kDirect, SG>(tok, grid, block, lds, st, a);
     }
 }
 
@@ -814,7 +910,7 @@ int gemv_fused_form(int xm, int M, int K) {
 
 // Picks the form and launches.  Returns false (nothing launched) if a fused
 // form was asked for and does not fit.
-template <int AM, bool INT_OUT>
+template <int AM, bool INT_OUT, int SG = 128>
 bool gemv_launch(GemvArgs a, hipStream_t st) {
     int nw, per;
     gemv_split(a.K, &nw, &per);
@@ -845,14 +941,14 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
     const int tok = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     dim3 grid(a.N / (int)kTileN), block(kWave * (nw + a.qw));
     switch (nb) {
-        case 1: gemv_launch_form<AM, 1, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 2: gemv_launch_form<AM, 2, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 3: gemv_launch_form<AM, 3, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 4: gemv_launch_form<AM, 4, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 5: gemv_launch_form<AM, 5, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 6: gemv_launch_form<AM, 6, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        case 7: gemv_launch_form<AM, 7, INT_OUT>(form, tok, grid, block, lds, st, a); break;
-        default: gemv_launch_form<AM, 8, INT_OUT>(form, tok, grid, block, lds, st, a); break;
+        case 1: gemv_launch_form<AM, 1, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 2: gemv_launch_form<AM, 2, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 3: gemv_launch_form<AM, 3, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 4: gemv_launch_form<AM, 4, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 5: gemv_launch_form<AM, 5, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 6: gemv_launch_form<AM, 6, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        case 7: gemv_launch_form<AM, 7, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
+        default: gemv_launch_form<AM, 8, INT_OUT, SG>(form, tok, grid, block, lds, st, a); break;
     }
     return true;
 }
@@ -867,12 +963,16 @@ void quant_launch(const void *x, int M, int K, int8_t *q, float *s_a, hipStream_
     else hipLaunchKernelGGL((quant_act_kernel<XM, 0>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
 }
 
-template <int OUT>
+template <int OUT, int SG = 128>
 void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float *sa, void *y, int M, int N, int K,
                  hipStream_t st) {
     const int ntm = (M + kGemmBM - 1) / kGemmBM, ntn = (N + kGemmBN - 1) / kGemmBN;
-    hipLaunchKernelGGL((gemm_kernel<OUT>), dim3(ntm * ntn), dim3(kGemmThreads), 0, st, p, s, q, sa, y, M, N, K, ntm);
+    hipLaunchKernelGGL((gemm_kernel<OUT, SG>), dim3(ntm * ntn), dim3(kGemmThreads), 0, st, p, s, q, sa, y, M, N, K,
+                       ntm);
 }
+
+// Integer sums over all of K are held as 64 * sum in int32: |64 * 127 * K| < 2^31.
+constexpr int kMaxIntK = 262144;
 
 bool gemm_grid_ok(int M) { return (int64_t)((M + kGemmBM - 1) / kGemmBM) * 65536 < ((int64_t)1 << 31); }
 
@@ -938,6 +1038,41 @@ bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, con
     return launched();
 }
 
+bitnet_status_t bitnet_w2a8_gemv_g(const uint8_t *packed, const float *scales, const int8_t *q, const float *s_a,
+                                   float *y, int M, int N, int K, int scale_block, hipStream_t stream) {
+    if (scale_block == 128) return bitnet_w2a8_gemv(packed, scales, q, s_a, y, M, N, K, stream);
+    if (scale_block != 64 && scale_block != 0) return BITNET_ERR_INVALID_ARG;
+    if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 4))
+        return BITNET_ERR_INVALID_ARG;
+    if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (scale_block == 0 && K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    GemvArgs a{packed, scales, q, s_a, y, nullptr, nullptr, nullptr, M, N, K, 0, 0, 0};
+    if (scale_block == 64) gemv_launch<-1, false, 64>(a, stream);
+    else gemv_launch<-1, false, 0>(a, stream);
+    return launched();
+}
+
+bitnet_status_t bitnet_w2a8_gemm_g(const uint8_t *packed, const float *scales, const int8_t *q, const float *s_a,
+                                   void *y, int ydt, int M, int N, int K, int scale_block, hipStream_t stream) {
+    if (scale_block == 128) return bitnet_w2a8_gemm(packed, scales, q, s_a, y, ydt, M, N, K, stream);
+    if (scale_block != 64 && scale_block != 0) return BITNET_ERR_INVALID_ARG;
+    if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
+        return BITNET_ERR_INVALID_ARG;
+    if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (scale_block == 0 && K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (scale_block == 64) {
+        if (ydt == BITNET_DT_BF16) gemm_launch<0, 64>(packed, scales, q, s_a, y, M, N, K, stream);
+        else gemm_launch<1, 64>(packed, scales, q, s_a, y, M, N, K, stream);
+    } else {
+        if (ydt == BITNET_DT_BF16) gemm_launch<0, 0>(packed, scales, q, s_a, y, M, N, K, stream);
+        else gemm_launch<1, 0>(packed, scales, q, s_a, y, M, N, K, stream);
+    }
+    return launched();
+}
+
 bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales, const void *x, int xdt,
                                      float *y, int8_t *q_out, float *s_a_out, int M, int N, int K,
                                      hipStream_t stream) {
@@ -966,8 +1101,7 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
                                     hipStream_t stream) {
     if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 16))
         return BITNET_ERR_INVALID_ARG;
-    // the int32 accumulators hold 64 * sum: |64 * 127 * K| < 2^31
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M) || K > 262144) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M) || K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (M <= kGemvMaxM) {
         GemvArgs a{packed, nullptr, q, nullptr, nullptr, acc, nullptr, nullptr, M, N, K, 0, 0, 0};
         gemv_launch<-1, true>(a, stream);

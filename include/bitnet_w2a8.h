@@ -133,6 +133,45 @@ bitnet_status_t bitnet_repack_i2s(const uint8_t *i2s, const float *scales, int64
 bitnet_status_t bitnet_unpack_i2s(const uint8_t *packed, const float *scales_tiled, int64_t N, int64_t K,
                                   int8_t *ternary_out, float *scales_out);
 
+/* ---------------------------------------------------------------- format variants, host */
+
+/* Scale granularity ([P3] "What i2_s actually is": blocks of 128 weights on x86
+ * and of 64 on ARM, one float scale per block): scale_block = 128 (the format of
+ * every function without the _g suffix), 64, or 0 for one fp32 scale for the
+ * whole matrix (the reading in which the scale multiplies the complete integer
+ * sum once).  The packed 2-bit tile layout is the same for all three; only the
+ * scales differ.  Tiled scale order: 128: [tile][block][16 rows]; 64: [tile]
+ * [128-block][16 rows][2 halves] (half h covers weights 128b + 64h .. +63);
+ * 0: the one value.  A scale_block outside {0, 64, 128} gives
+ * BITNET_ERR_INVALID_ARG (or 0 from bitnet_scale_count_g). */
+
+/* Number of fp32 scales: N*K/scale_block, 1 for scale_block 0; 0 if the shape
+ * or scale_block is unsupported. */
+size_t bitnet_scale_count_g(int64_t N, int64_t K, int scale_block);
+
+/* absmean ternarisation at granularity scale_block: per block of 64 or 128
+ * weights as bitnet_ternarize_absmean; for 0, gamma = (sum of |w| over the whole
+ * matrix in fp64, row-major order) / (N*K) rounded to fp32, scales[0] = gamma.
+ *   scales  host, fp32 [N][K/scale_block] row-major, or one value (out) */
+bitnet_status_t bitnet_ternarize_absmean_g(const float *w, int64_t N, int64_t K, int scale_block,
+                                           int8_t *ternary, float *scales);
+
+/* bitnet_pack_i2s with scales [N][K/scale_block] row-major (one value for 0);
+ * scales_out holds bitnet_scale_count_g(N, K, scale_block) fp32. */
+bitnet_status_t bitnet_pack_i2s_g(const int8_t *ternary, const float *scales, int64_t N, int64_t K,
+                                  int scale_block, uint8_t *packed_out, float *scales_out);
+
+/* bitnet_repack_i2s for canonical bytes of the given format: for scale_block 64
+ * byte j of 64-block b holds weights 64b + 16g + j (g = 0 in bits 7..6; the
+ * 128-block rule scaled to 64 weights, a reading); for 128 and 0 the 128-block
+ * canonical bytes. */
+bitnet_status_t bitnet_repack_i2s_g(const uint8_t *i2s, const float *scales, int64_t N, int64_t K,
+                                    int scale_block, uint8_t *packed_out, float *scales_out);
+
+/* Inverse of bitnet_pack_i2s_g (host). */
+bitnet_status_t bitnet_unpack_i2s_g(const uint8_t *packed, const float *scales_tiled, int64_t N, int64_t K,
+                                    int scale_block, int8_t *ternary_out, float *scales_out);
+
 /* ---------------------------------------------------------------- device, async */
 
 /* Per-token absmax int8 quantisation of activations ([P2] "Architecture
@@ -204,6 +243,19 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
 bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, const int8_t *q,
                                  const float *s_a, void *y, int ydt, int M, int N, int K,
                                  hipStream_t stream);
+
+/* bitnet_w2a8_gemv / bitnet_w2a8_gemm at scale granularity scale_block (tiled
+ * scales from bitnet_pack_i2s_g).  For 64: y = s_a * sum over 64-blocks of
+ * S * A (fp32, order unspecified, same tolerance as bitnet_w2a8_gemv).  For 0:
+ * the exact int32 sum over all of K, converted to fp32 and multiplied by
+ * (s_a * S) (two fp32 roundings).  Rules: as the 128 versions; scale_block 0
+ * also needs K <= 262144. */
+bitnet_status_t bitnet_w2a8_gemv_g(const uint8_t *packed, const float *scales, const int8_t *q,
+                                   const float *s_a, float *y, int M, int N, int K, int scale_block,
+                                   hipStream_t stream);
+bitnet_status_t bitnet_w2a8_gemm_g(const uint8_t *packed, const float *scales, const int8_t *q,
+                                   const float *s_a, void *y, int ydt, int M, int N, int K, int scale_block,
+                                   hipStream_t stream);
 
 /* One layer of a chain of products (see bitnet_w2a8_chain). */
 typedef struct {

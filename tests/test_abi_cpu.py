@@ -173,3 +173,61 @@ def test_junction_codes():
     for bad in ("relu", 3, -1, 2.5):
         with pytest.raises(ValueError):
             bn.junction_code(bad)
+
+
+# ------------------------------------------------------------------ scale granularity (host side)
+@pytest.mark.parametrize("G", [0, 64])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 2560)])
+def test_ternarize_g_matches_oracle(G, N, K):
+    W = wl.rng_for(91, G, N, K).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    T, S = bn.bitnet_ternarize_absmean_g(W, G)
+    To, So = oracle.ternarize_absmean_g(W, G)
+    assert np.array_equal(T, To) and np.array_equal(S, So)
+
+
+def test_ternarize_g0_config2_shape_matches_oracle():
+    # one gamma over 35 M weights: the fp64 sum runs in the same row-major order on both sides
+    W = wl.rng_for(92).normal(0, 0.02, size=(13824, 2560)).astype(np.float32)
+    T, S = bn.bitnet_ternarize_absmean_g(W, 0)
+    To, So = oracle.ternarize_absmean_g(W, 0)
+    assert S[0] == So[0] and np.array_equal(T, To)
+
+
+@pytest.mark.parametrize("G", [0, 64, 128])
+@pytest.mark.parametrize("N,K", [(16, 128), (80, 640), (2560, 2560)])
+def test_pack_g_roundtrip_and_repack_from_canonical(G, N, K):
+    r = wl.rng_for(93, G, N, K)
+    T = wl.ternary_uniform(r, N, K)
+    S = r.uniform(0.5, 2, size=oracle.scale_shape(N, K, G)).astype(np.float32)
+    p, st = bn.bitnet_pack_i2s_g(T, S, G)
+    assert st.size == bn.bitnet_scale_count_g(N, K, G) == (1 if G == 0 else N * K // G)
+    T2, S2 = bn.bitnet_unpack_i2s_g(p, st, N, K, G)
+    assert np.array_equal(T2, T) and np.array_equal(S2, S)
+    # the packed weights do not depend on the scale granularity
+    assert np.array_equal(p, bn.bitnet_pack_i2s(T, np.ones((N, K // 128), np.float32))[0])
+    p3, st3 = bn.bitnet_repack_i2s_g(oracle.pack_i2s_g(T, G), S, K, G)
+    assert np.array_equal(p3, p) and np.array_equal(st3, st)
+
+
+def test_tiled_scale_order_g64():
+    # [tile][128-block][16 rows][2 halves]: the scale of row n, 64-block c sits at
+    # (((n // 16) * (K // 128) + c // 2) * 16 + n % 16) * 2 + c % 2
+    N, K = 32, 384
+    S = np.arange(N * K // 64, dtype=np.float32).reshape(N, K // 64)
+    _, st = bn.bitnet_pack_i2s_g(np.zeros((N, K), np.int8), S, 64)
+    for n in range(N):
+        for c in range(K // 64):
+            assert st[(((n // 16) * (K // 128) + c // 2) * 16 + n % 16) * 2 + c % 2] == S[n, c]
+
+
+def test_g_variants_reject_bad_scale_block():
+    T = np.zeros((16, 128), np.int8)
+    assert bn.bitnet_scale_count_g(16, 128, 32) == 0
+    st = bn.lib().bitnet_pack_i2s_g(T.ctypes.data, np.ones(4, np.float32).ctypes.data, 16, 128, 32,
+                                    np.empty(512, np.uint8).ctypes.data, np.empty(64, np.float32).ctypes.data)
+    assert st == bn.BITNET_ERR_INVALID_ARG
+    for sb in (32, 96, -1):
+        assert bn.lib().bitnet_w2a8_gemv_g(None, None, None, None, None, 1, 16, 128, sb, None) == \
+            bn.BITNET_ERR_INVALID_ARG
+        assert bn.lib().bitnet_w2a8_gemm_g(None, None, None, None, None, 0, 1, 16, 128, sb, None) == \
+            bn.BITNET_ERR_INVALID_ARG
