@@ -565,6 +565,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 // ordered so that the token tiles sharing a weight tile run on one XCD (one
 // L2) when the grid divides evenly over the 8 XCDs.
 // ==========================================================================
+// Empty asm that takes a value in and out of a VGPR: an ordering point that
+// pure arithmetic (matrix-core steps, the fp32 drain) cannot be moved across.
+__device__ __forceinline__ void keep(float &x) { asm volatile("" : "+v"(x)); }
+
 constexpr int kGemmBM = 128, kGemmBN = 256, kGemmThreads = 512;
 constexpr int kAStride = 144;                        // padded LDS row of the activation tile
 constexpr int kAStage = kGemmBM * kAStride;          // 18432 bytes
@@ -727,16 +731,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
                 for (int e = 0; e < 4; ++e) yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
     };
 
-    // Waves w and w + 4 share a SIMD.  With a barrier per block both would run
-    // their VALU phases (decode, drain) and their matrix-core phases at the same
-    // time; the upper four waves therefore drain each block one iteration late
-    // (accumulators and scales held in registers across the barrier), so that
-    // one wave's drain overlaps its partner's matrix-core steps.
-    const bool lag = w >= 4;
     v4i cl[4][4];
     float scl[4][4];
 
-    auto compute = [&](int st, bool first) {
+    auto compute = [&](int st) {
         v4i ao[4][2], bw[4][2];
         if constexpr (SG == 64 && BLOCKED) {
             // one scale per matrix-core step (64 weights): each half's 16 steps are
@@ -750,17 +748,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
 #pragma unroll
                     for (int tj = 0; tj < 4; ++tj) cl[ti][tj] = mfma_i8(bw[tj][h], ao[ti][h], v4i{0, 0, 0, 0});
                 drain(cl, scl);
-                __builtin_amdgcn_sched_barrier(0);  // one set of accumulators live
+                if (h == 0) {  // finish the first half's drain before the second half's steps
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                        for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) keep(yacc[ti][tj][e]);
+                }
             }
         } else if constexpr (!BLOCKED) {  // integer sums over all of K
             operands(st, ao, bw);
             mma(ao, bw, iacc, false);
-        } else {  // both orders use the same accumulator and scale registers
-            if (lag && !first) drain(cl, scl);  // the previous block, then start this one
+        } else {
             operands(st, ao, bw);
             load_sc(st, 0, scl);
             mma(ao, bw, cl, true);
-            if (!lag) drain(cl, scl);
+            drain(cl, scl);
         }
     };
 
@@ -776,18 +780,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     // written out with fixed register sets (no pointer selects between them).
     for (int b = 0; b < nblk; b += 2) {
         gload(b + 2, r0);
-        compute(0, b == 0);
+        compute(0);
         lstore(1, r1);
         lds_barrier();
         if (b + 1 < nblk) {
             gload(b + 3, r1);
-            compute(1, false);
+            compute(1);
             lstore(0, r0);
             lds_barrier();
         }
-    }
-    if constexpr (SG != 64 && BLOCKED) {
-        if (lag) drain(cl, scl);  // the last block of the lagging waves
     }
 
     // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j,
