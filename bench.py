@@ -38,9 +38,9 @@ ROTATE_BYTES = 2 * LLC_BYTES
 # what the counter reads for a 64 MiB device copy (FETCH_SIZE x 1.999,
 # WRITE_SIZE x 1.000).  Valid only for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha1": "3f8dd9235507477ffaff5fa3e5e9989f64bbc5da",
-    "bytes_per_launch": 10075000,
-    "fetch_kib": 4895.0, "write_kib": 54.0, "fetch_scale": 1.999, "write_scale": 1.000,
+    "kernel_source_sha1": "5584a2bd48fef1ab0fc23a9e92b94b3db52ac1e7",
+    "bytes_per_launch": 10075839,
+    "fetch_kib": 4895.1, "write_kib": 54.0, "fetch_scale": 1.999, "write_scale": 1.000,
 }
 
 
@@ -223,30 +223,88 @@ def prefill_shape(torch, bn, wl, reps=10):
     }
 
 
-def stack_shape(torch, bn, wl, Ms=(1, 8), reps=20):
+def stack_shape(torch, bn, wl, runs=((1, "sum"), (8, "sum"), (1, "relu2_glu")), reps=20):
     """The 30-layer decode stack (4 x 2560x2560, 13824x2560, 2560x6912 per layer):
-    one token = one bitnet_w2a8_chain call (180 products), captured as a graph."""
+    one token = one bitnet_w2a8_chain call (180 products), captured as a graph.
+    The junction in front of each 2560x6912 layer is the linear fold (the
+    headline stack) or the squared-ReLU gate."""
     t0 = time.perf_counter()
-    ws, folds, pbytes = [], [], 0
+    ws, pbytes = [], 0
     for layer in range(wl.STACK_LAYERS):
         for idx in range(6):
             T, S = wl.stack_matrix(layer, idx)
             ws.append(bn.PackedWeight.from_ternary(T, S))
-            folds.append(idx == 5)
             pbytes += T.size // 4
-    chain = bn.Chain(ws, folds)
     setup_s = time.perf_counter() - t0
     out = []
-    for M in Ms:
+    for M, junction in runs:
+        chain = bn.Chain(ws, [junction if i % 6 == 5 else False for i in range(len(ws))])
         x = torch.from_numpy(wl.stack_input(M).view(np.int16)).cuda().view(torch.bfloat16)
         y = torch.empty((M, wl.STACK_HIDDEN), dtype=torch.float32, device="cuda")
         chain.workspace(M)
         us = graph_us_per_launch(torch, lambda i: chain(x, y=y), 1, reps)
-        out.append({"shape": "stack_30x6_decode", "M": M, "token_step_us": us, "tokens_per_s": M * 1e6 / us,
-                    "products_per_token": len(ws), "packed_bytes_per_token": pbytes,
+        out.append({"shape": "stack_30x6_decode", "M": M, "junction": junction, "token_step_us": us,
+                    "tokens_per_s": M * 1e6 / us, "products_per_token": len(ws), "packed_bytes_per_token": pbytes,
                     "packed_GBps": pbytes / us / 1e3, "pct_hbm_packed": 100.0 * pbytes / us / 1e3 / HBM_PEAK_GBS,
                     "setup_s": setup_s})
-    del chain, ws
+        del chain
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def format_shapes(torch, bn, wl, reps=10):
+    """Scale-granularity variants (64-weight blocks, one scale per matrix) of the
+    13824x2560 decode product (M=1, rotated weights) and the 512-token prefill."""
+    c = wl.config4()
+    x = torch.from_numpy(c.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    q, sa = bn.bitnet_quant_act(x)
+    q1, sa1 = q[:1].contiguous(), sa[:1].contiguous()
+    r = wl.rng_for(4, 7)
+    out = []
+    for G in (64, 0):
+        S = r.uniform(0.5, 2, size=(1,) if G == 0 else (c.N, c.K // G)).astype(np.float32)
+        packed, st = bn.bitnet_pack_i2s_g(c.T, S, G)
+        nrot = max(2, math.ceil(ROTATE_BYTES / (packed.nbytes + st.nbytes)))
+        P = [torch.from_numpy(packed).cuda() for _ in range(nrot)]
+        Sd = [torch.from_numpy(st).cuda() for _ in range(nrot)]
+        y1 = torch.empty((1, c.N), dtype=torch.float32, device="cuda")
+        gemv_us = graph_us_per_launch(torch, lambda i: bn.bitnet_w2a8_gemv_g(P[i % nrot], Sd[i % nrot], q1, sa1, c.N,
+                                                                              c.K, G, y=y1), nrot, reps)
+        yb = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        gemm_us = graph_us_per_launch(torch, lambda i: bn.bitnet_w2a8_gemm_g(P[0], Sd[0], q, sa, c.N, c.K, G, y=yb),
+                                      20, reps)
+        ops = 2.0 * c.M * c.N * c.K
+        out.append({"shape": "formats_13824x2560", "scale_block": G, "gemv_m1_us": gemv_us,
+                    "gemv_packed_GBps": c.N * c.K / 4 / gemv_us / 1e3, "gemm_m512_us": gemm_us,
+                    "gemm_int8_mfma_pct": 100.0 * ops / gemm_us / 1e6 / INT8_MFMA_PEAK_TOPS})
+        del P, Sd
+        torch.cuda.empty_cache()
+    return out
+
+
+def medium_batch_shapes(torch, bn, wl, reps=10):
+    """13824x2560 between decode and prefill: the decode kernel up to M=16, the
+    prefill kernel from M=16 to 128 (weights rotated through HBM for both)."""
+    c = wl.config4()
+    x = torch.from_numpy(c.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    q, sa = bn.bitnet_quant_act(x)
+    rot = Rotation(torch, *bn.bitnet_pack_i2s(c.T, c.S))
+    pbytes = c.N * c.K // 4
+    out = []
+    for M in (16, 32, 64, 128):
+        qm, sm = q[:M].contiguous(), sa[:M].contiguous()
+        row = {"shape": "medium_batch_13824x2560", "M": M}
+        if M <= 16:
+            y = torch.empty((M, c.N), dtype=torch.float32, device="cuda")
+            us = graph_us_per_launch(torch, lambda i: bn.bitnet_w2a8_gemv(*rot[i], qm, sm, c.N, c.K, y=y), rot.R, reps)
+            row.update({"gemv_us": us, "gemv_packed_GBps": pbytes / us / 1e3})
+        yb = torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda")
+        us = graph_us_per_launch(torch, lambda i: bn.bitnet_w2a8_gemm(*rot[i], qm, sm, c.N, c.K, y=yb), rot.R, reps)
+        row.update({"gemm_us": us, "gemm_packed_GBps": pbytes / us / 1e3,
+                    "gemm_int8_TOPS": 2.0 * M * c.N * c.K / us / 1e6})
+        out.append(row)
+    del rot
     torch.cuda.empty_cache()
     return out
 
@@ -422,6 +480,9 @@ def main():
         r = prefill_shape(torch, bn, wl)
         log(json.dumps(r))
         shapes.append(r)
+        for r in format_shapes(torch, bn, wl) + medium_batch_shapes(torch, bn, wl):
+            log(json.dumps(r))
+            shapes.append(r)
         for r in stack_shape(torch, bn, wl):
             log(json.dumps(r))
             shapes.append(r)
