@@ -553,15 +553,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 
 // ==========================================================================
 // a6: prefill product, any M.  A 512-thread workgroup owns a 128-token x
-// 256-row output tile; wave (wm, wn) = (w / 4, w % 4) owns 64 tokens x 64 rows
-// = 4 x 4 matrix-core tiles.  Per 128-weight block the workgroup stages the
-// block's activations (128 x 128 int8, rows padded to 144 bytes so the
-// operand reads are conflict-free), its 16 packed bricks (8 KB) and 256
+// 64*RT-row output tile (RT = 4 normally; 2 or 1 when few tokens would leave
+// the chip short of workgroups); wave (wm, wn) = (w / 4, w % 4) owns 64 tokens
+// x 16*RT rows = 4 x RT matrix-core tiles.  Per 128-weight block the workgroup
+// stages the block's activations (128 x 128 int8, rows padded to 144 bytes so
+// the operand reads are conflict-free), its 4*RT packed bricks and their
 // scales in LDS with two or three coalesced 16-byte loads per thread; the
 // next block's loads are in flight while the current block computes (double
-// buffer, one barrier per block).  Each wave decodes its 4 row-tiles once per
-// block and reuses them for its 4 token-tiles (32 matrix-core steps), then
-// drains the int32 tiles into fp32 with the block scales.  Workgroups are
+// buffer, one barrier per block).  Each wave decodes its RT row-tiles once per
+// block and reuses them for its 4 token-tiles, then drains the int32 tiles
+// into fp32 with the block scales.  Workgroups are
 // ordered so that the token tiles sharing a weight tile run on one XCD (one
 // L2) when the grid divides evenly over the 8 XCDs.
 // ==========================================================================
@@ -569,11 +570,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 // pure arithmetic (matrix-core steps, the fp32 drain) cannot be moved across.
 __device__ __forceinline__ void keep(float &x) { asm volatile("" : "+v"(x)); }
 
-constexpr int kGemmBM = 128, kGemmBN = 256, kGemmThreads = 512;
+constexpr int kGemmBM = 128, kGemmThreads = 512;
 constexpr int kAStride = 144;                        // padded LDS row of the activation tile
 constexpr int kAStage = kGemmBM * kAStride;          // 18432 bytes
-constexpr int kBStage = (kGemmBN / 16) * 512;        // 8192 bytes: 16 bricks
-constexpr int kSStage = kGemmBN * 4;                 // 1024 bytes: [16 tiles][16 rows] fp32 (x2 for 64-blocks)
+constexpr int kBStage = 16 * 512;                    // 8192 bytes: up to 16 bricks
+constexpr int kSStage = 16 * 16 * 4;                 // 1024 bytes: [16 tiles][16 rows] fp32 (x2 for 64-blocks)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -585,7 +586,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // weights per scale (scales staged per block: [tile][16 rows] or
 // [tile][16 rows][2 halves]) or 0 (one scale: integer sums over all of K,
 // scaled once in the epilogue).
-template <int OUT, int SG>
+template <int OUT, int SG, int RT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                              const float *__restrict__ scales,
                                                              const int8_t *__restrict__ q,
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     int t = blockIdx.x;
     if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // XCD-aware order
     const int tm = t % ntm, tn = t / ntm;
-    const int m0 = tm * kGemmBM, T0 = tn * (kGemmBN / 16);
+    const int m0 = tm * kGemmBM, T0 = tn * (4 * RT);  // RT row tiles per wave, 4 waves across
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, j = l & 15;
@@ -620,13 +621,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         aok[r] = tok < M;
         aptr[r] = q + (size_t)(aok[r] ? tok : 0) * K + acol[r];
     }
-    const int bT = T0 + (tid >> 5);
+    const int bT = T0 + min(tid >> 5, 4 * RT - 1);  // threads past the tile's bricks repeat the last
     const bool bok = bT < ntile_n;
     const uint8_t *bptr = packed + (size_t)(bok ? bT : 0) * nblk * kBrickBytes + (tid & 31) * 16;
     // scale staging: 64 (SG 128) or 128 (SG 64) threads, one float4 each per block
     constexpr int SCT = 4 * SPT;  // staging threads per tile
-    // threads past the 16 tiles' scales repeat the last tile's (not stored)
-    const int sT = T0 + min(tid / SCT, 15);
+    // threads past the 4*RT tiles' scales repeat the last tile's (not stored)
+    const int sT = T0 + min(tid / SCT, 4 * RT - 1);
     const bool sok = BLOCKED && sT < ntile_n;
     const float *sptr = scales + (size_t)(sok ? sT : 0) * nblk * kTileN * SPT + (tid % SCT) * 4;
 
@@ -654,9 +655,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(base + arow[i] * kAStride + acol[i]) = r.a[i];
-        *reinterpret_cast<v4i *>(base + kAStage + tid * 16) = r.b;
+        if (tid < 128 * RT) *reinterpret_cast<v4i *>(base + kAStage + tid * 16) = r.b;
         // LDS scales: [half][16 tiles][16 rows]; global SG 64 order is [tile][row][half]
-        if (BLOCKED && tid < 16 * SCT) {
+        if (BLOCKED && tid < 4 * RT * SCT) {
             float *sb = reinterpret_cast<float *>(base + kAStage + kBStage);
             if constexpr (SG == 128) {
                 *reinterpret_cast<v4f *>(sb + 4 * tid) = r.s;
@@ -668,21 +669,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         }
     };
 
-    float yacc[4][4][4];
-    v4i iacc[4][4];  // unscaled paths: the matrix core accumulates over all of K
+    float yacc[4][RT][4];
+    v4i iacc[4][RT];  // unscaled paths: the matrix core accumulates over all of K
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < RT; ++b) {
             iacc[a][b] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 4; ++e) yacc[a][b][e] = 0.0f;
         }
 
     // Operands of one block: activation fragments of the wave's 4 token tiles and
-    // the decoded weights of its 4 row tiles (matrix-core A = weights (rows),
+    // the decoded weights of its RT row tiles (matrix-core A = weights (rows),
     // B = activations (tokens): lane (g, j) receives rows 4g..4g+3 of token j).
-    auto operands = [&](int st, v4i (&ao)[4][2], v4i (&bw)[4][2]) {
+    auto operands = [&](int st, v4i (&ao)[4][2], v4i (&bw)[RT][2]) {
         const unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -690,52 +691,52 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
             for (int s = 0; s < 2; ++s)
                 ao[ti][s] = *reinterpret_cast<const v4i *>(base + (64 * wm + 16 * ti + j) * kAStride + 64 * s + 16 * g);
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + (4 * wn + tj) * 512 + l * 8);
+        for (int tj = 0; tj < RT; ++tj) {
+            const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + (RT * wn + tj) * 512 + l * 8);
             bw[tj][0] = decode16(wv.x);
             bw[tj][1] = decode16(wv.y);
         }
     };
-    // scales of rows 4g..4g+3 of the wave's 4 row tiles, for half h
-    auto load_sc = [&](int st, int h, float (&sc)[4][4]) {
+    // scales of rows 4g..4g+3 of the wave's RT row tiles, for half h
+    auto load_sc = [&](int st, int h, float (&sc)[RT][4]) {
         const unsigned char *base = lds + st * STAGE;
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
+        for (int tj = 0; tj < RT; ++tj) {
             const float4 s4 = *reinterpret_cast<const float4 *>(base + kAStage + kBStage + h * 1024 +
-                                                                ((4 * wn + tj) * 16 + 4 * g) * 4);
+                                                                ((RT * wn + tj) * 16 + 4 * g) * 4);
             sc[tj][0] = s4.x;
             sc[tj][1] = s4.y;
             sc[tj][2] = s4.z;
             sc[tj][3] = s4.w;
         }
     };
-    // the 16 tiles' first K-steps are independent and pipeline on the matrix
+    // the 4 x RT tiles' first K-steps are independent and pipeline on the matrix
     // core; the second K-steps then find their accumulators long finished
-    auto mma = [&](const v4i (&ao)[4][2], const v4i (&bw)[4][2], v4i (&c)[4][4], bool from_zero) {
+    auto mma = [&](const v4i (&ao)[4][2], const v4i (&bw)[RT][2], v4i (&c)[4][RT], bool from_zero) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < RT; ++tj)
                 c[ti][tj] = mfma_i8(bw[tj][0], ao[ti][0], from_zero ? v4i{0, 0, 0, 0} : c[ti][tj]);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) c[ti][tj] = mfma_i8(bw[tj][1], ao[ti][1], c[ti][tj]);
+            for (int tj = 0; tj < RT; ++tj) c[ti][tj] = mfma_i8(bw[tj][1], ao[ti][1], c[ti][tj]);
     };
-    auto drain = [&](const v4i (&c)[4][4], const float (&sc)[4][4]) {
+    auto drain = [&](const v4i (&c)[4][RT], const float (&sc)[RT][4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < RT; ++tj)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
     };
 
-    v4i cl[4][4];
-    float scl[4][4];
+    v4i cl[4][RT];
+    float scl[RT][4];
 
     auto compute = [&](int st) {
-        v4i ao[4][2], bw[4][2];
+        v4i ao[4][2], bw[RT][2];
         if constexpr (SG == 64 && BLOCKED) {
             // one scale per matrix-core step (64 weights): each half's 16 steps are
             // drained with that half's scales, in the registers of the 128 path
@@ -746,13 +747,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                    for (int tj = 0; tj < 4; ++tj) cl[ti][tj] = mfma_i8(bw[tj][h], ao[ti][h], v4i{0, 0, 0, 0});
+                    for (int tj = 0; tj < RT; ++tj) cl[ti][tj] = mfma_i8(bw[tj][h], ao[ti][h], v4i{0, 0, 0, 0});
                 drain(cl, scl);
                 if (h == 0) {  // finish the first half's drain before the second half's steps
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                        for (int tj = 0; tj < 4; ++tj)
+                        for (int tj = 0; tj < RT; ++tj)
 #pragma unroll
                             for (int e = 0; e < 4; ++e) keep(yacc[ti][tj][e]);
                 }
@@ -778,21 +779,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     // the registers just freed.  Loads past the last block repeat it and their
     // LDS copy goes to a slot nobody reads again.  Both halves of the loop are
     // written out with fixed register sets (no pointer selects between them).
+    // Waves whose 64 tokens all lie past M only stage data (few-token launches).
+    const bool live = m0 + 64 * wm < M;
     for (int b = 0; b < nblk; b += 2) {
         gload(b + 2, r0);
-        compute(0);
+        if (live) compute(0);
         lstore(1, r1);
         lds_barrier();
         if (b + 1 < nblk) {
             gload(b + 3, r1);
-            compute(1);
+            if (live) compute(1);
             lstore(0, r0);
             lds_barrier();
         }
     }
 
     // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j,
-    // row 16(T0+4wn+tj)+4g+e: four consecutive outputs of one token per store
+    // row 16(T0+RT*wn+tj)+4g+e: four consecutive outputs of one token per store
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
         const int m = m0 + 64 * wm + 16 * ti + j;
@@ -801,8 +804,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         // sum times s_a * s_w
         const float f = (OUT == 2) ? 0.0f : BLOCKED ? s_a[m] * 0.015625f : s_a[m] * scales[0];
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            const int T = T0 + 4 * wn + tj;
+        for (int tj = 0; tj < RT; ++tj) {
+            const int T = T0 + RT * wn + tj;
             if (T >= ntile_n) continue;
             const size_t idx = (size_t)m * N + (size_t)T * 16 + 4 * g;
             float v[4];
@@ -964,18 +967,35 @@ void quant_launch(const void *x, int M, int K, int8_t *q, float *s_a, hipStream_
     else hipLaunchKernelGGL((quant_act_kernel<XM, 0>), dim3(M), dim3(256), 0, st, x, K, q, s_a);
 }
 
+// Row tiles per wave: 4 (256-row workgroup tiles) unless that leaves the chip
+// short of workgroups (few tokens), then 2 or 1 (128 / 64 rows).
+int gemm_row_tiles(int M, int N) {
+    const int ntm = (M + kGemmBM - 1) / kGemmBM;
+    for (int rt = 4; rt > 1; rt >>= 1)
+        if ((int64_t)ntm * ((N + 64 * rt - 1) / (64 * rt)) >= 200) return rt;
+    return 1;
+}
+
 template <int OUT, int SG = 128>
 void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float *sa, void *y, int M, int N, int K,
                  hipStream_t st) {
-    const int ntm = (M + kGemmBM - 1) / kGemmBM, ntn = (N + kGemmBN - 1) / kGemmBN;
-    hipLaunchKernelGGL((gemm_kernel<OUT, SG>), dim3(ntm * ntn), dim3(kGemmThreads), 0, st, p, s, q, sa, y, M, N, K,
-                       ntm);
+    const int ntm = (M + kGemmBM - 1) / kGemmBM, rt = gemm_row_tiles(M, N);
+    const int ntn = (N + 64 * rt - 1) / (64 * rt);
+    const dim3 grid(ntm * ntn), block(kGemmThreads);
+    if (rt == 4) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 4>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    else if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
 }
 
 // Integer sums over all of K are held as 64 * sum in int32: |64 * 127 * K| < 2^31.
 constexpr int kMaxIntK = 262144;
 
-bool gemm_grid_ok(int M) { return (int64_t)((M + kGemmBM - 1) / kGemmBM) * 65536 < ((int64_t)1 << 31); }
+// The launch's work-item count must fit the 32-bit grid size.
+bool gemm_grid_ok(int M, int N) {
+    const int rt = gemm_row_tiles(M, N);
+    const int64_t wgs = (int64_t)((M + kGemmBM - 1) / kGemmBM) * ((N + 64 * rt - 1) / (64 * rt));
+    return wgs * kGemmThreads < ((int64_t)1 << 32);
+}
 
 }  // namespace
 
@@ -1033,7 +1053,7 @@ bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, con
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N)) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (ydt == BITNET_DT_BF16) gemm_launch<0>(packed, scales, q, s_a, y, M, N, K, stream);
     else gemm_launch<1>(packed, scales, q, s_a, y, M, N, K, stream);
     return launched();
@@ -1062,7 +1082,7 @@ bitnet_status_t bitnet_w2a8_gemm_g(const uint8_t *packed, const float *scales, c
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N)) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (scale_block == 0 && K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (scale_block == 64) {
         if (ydt == BITNET_DT_BF16) gemm_launch<0, 64>(packed, scales, q, s_a, y, M, N, K, stream);
@@ -1102,7 +1122,7 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
                                     hipStream_t stream) {
     if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 16))
         return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M) || K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N) || K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (M <= kGemvMaxM) {
         GemvArgs a{packed, nullptr, q, nullptr, nullptr, acc, nullptr, nullptr, M, N, K, 0, 0, 0};
         gemv_launch<-1, true>(a, stream);

@@ -297,3 +297,29 @@ def test_config4_gemm_full_sampled(gpu):
     ref = oracle.w2a8(oracle.pack_i2s(c.T[rows]), c.S[rows], qo[toks], so[toks], len(rows), c.K)
     assert np.array_equal(acc[np.ix_(toks, rows)], ref["acc"])
     assert_bf16_ok(ybits[np.ix_(toks, rows)], ref, "config4 sampled")
+
+
+# ------------------------------------------------------------------ prefill row-tile choices
+# Few-token launches use narrower workgroup tiles (256 -> 128 -> 64 rows) so that the
+# grid still fills the chip: 64 x 13824 and 512 x 2560 take 64-row tiles, 256 x 13824
+# takes 128-row tiles, 512 x 13824 the full 256 rows.
+@pytest.mark.parametrize("M,N,K", [(64, 13824, 2560), (256, 13824, 2560), (512, 2560, 6912), (40, 2576, 640)])
+def test_gemm_row_tile_choices_sampled(gpu, M, N, K):
+    c = wl.small_case(M + N + K, M, N, K)
+    p, st = pack_dev(c.T, c.S)
+    qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    yb = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, N, K).view(torch.int16)).view(np.uint16)
+    y32 = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, N, K,
+                                   y=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")))
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, N, K))
+    r = wl.rng_for(97, M, N, K)
+    toks = np.sort(r.choice(M, min(M, 12), replace=False))
+    tiles = np.sort(r.choice(N // 16, min(N // 16, 16), replace=False))
+    rows = (tiles[:, None] * 16 + np.arange(16)).ravel()
+    ref = oracle.w2a8(oracle.pack_i2s(c.T[rows]), c.S[rows], qo[toks], so[toks], rows.size, K)
+    assert np.array_equal(acc[np.ix_(toks, rows)], ref["acc"])
+    assert_f32_close(y32[np.ix_(toks, rows)], ref, f"gemm f32 {M}x{N}x{K}")
+    assert_bf16_ok(yb[np.ix_(toks, rows)], ref, f"gemm bf16 {M}x{N}x{K}")
+    # every output element is written (the buffer started as NaN)
+    assert np.isfinite(y32).all()
