@@ -779,8 +779,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     // the registers just freed.  Loads past the last block repeat it and their
     // LDS copy goes to a slot nobody reads again.  Both halves of the loop are
     // written out with fixed register sets (no pointer selects between them).
-    // Waves whose 64 tokens all lie past M only stage data (few-token launches).
-    const bool live = m0 + 64 * wm < M;
+    // Waves whose 64 tokens all lie past M only stage data (few-token launches,
+    // which take RT < 4; the 256-row form keeps a branch-free loop).
+    const bool live = RT == 4 || m0 + 64 * wm < M;
     for (int b = 0; b < nblk; b += 2) {
         gload(b + 2, r0);
         if (live) compute(0);

@@ -323,3 +323,28 @@ def test_gemm_row_tile_choices_sampled(gpu, M, N, K):
     assert_bf16_ok(yb[np.ix_(toks, rows)], ref, f"gemm bf16 {M}x{N}x{K}")
     # every output element is written (the buffer started as NaN)
     assert np.isfinite(y32).all()
+
+
+# ------------------------------------------------------------------ the largest K
+def test_max_k_integer_sums_do_not_overflow(gpu):
+    # the int32 accumulators hold 64 x the integer sum: at the largest K with every
+    # weight +1 and every activation 127 the sum is 127 * 262144 = 33,292,288 and
+    # 64 x that = 2,130,706,432 < 2^31; one block more is rejected
+    K = 262144
+    N, M = 16, 2
+    T = np.ones((N, K), np.int8)
+    T[1::2] = -1
+    p, st = pack_dev(T, np.ones((N, K // 128), np.float32))
+    q = np.full((M, K), 127, np.int8)
+    q[1] = -127
+    qd = dev(q)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, N, K))
+    want = np.where(np.arange(N)[None, :] % 2 == 0, 1, -1) * np.array([[127], [-127]]) * K
+    assert np.array_equal(acc, want.astype(np.int32))
+    # the fp32 product through the same kernels: unit scales, s_a = 1 -> y == acc exactly
+    y = host(bn.bitnet_w2a8_gemv(p, st, qd, dev(np.ones(M, np.float32)), N, K))
+    assert np.array_equal(y, want.astype(np.float32))
+    pb, sb = pack_dev(np.ones((N, K + 128), np.int8), np.ones((N, (K + 128) // 128), np.float32))
+    with pytest.raises(bn.BitnetError) as ei:
+        bn.bitnet_w2a8_acc_i32(pb, dev(np.ones((M, K + 128), np.int8)), N, K + 128)
+    assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
