@@ -11,9 +11,11 @@ twice the 256 MB last-level cache, so the weight stream comes from HBM.
 value = packed-weight bytes (N*K/4) per step / step time, in GB/s.
 The roofline object prices the product kernel against 8 TB/s using its
 algorithmic bytes (packed weights + fp32 block scales + int8 activations +
-fp32 outputs) over its own duration, measured with HIP events around each
-launch on the launch stream.  Per-shape results for every decode shape, the
-prefill product and the decode stack are reported under "shapes".
+fp32 outputs) over its own duration, measured with HIP events around graph
+replays on the launch stream; beside it, "attainable_read" is what one bare
+pass of 16-byte loads over the same number of bytes achieves on this GPU.
+Per-shape results for every decode shape, the prefill product, the format
+variants, the medium batches and the decode stack are reported under "shapes".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
 """
@@ -194,6 +196,23 @@ class DecodeShape:
             "packed_pct_hbm_gemv": 100.0 * pb / gemv_us / 1e3 / HBM_PEAK_GBS,
             "alg_GBps_gemv": ab / gemv_us / 1e3, "alg_bytes": ab,
         }
+
+
+def attainable_read(torch, bn, nbytes, reps=10):
+    """Graph-timed plain stream read (bitnet_probe_stream_read) of nbytes, rounded
+    up to 16, cycling through copies larger than twice the last-level cache: what
+    a bare one-pass read of the product kernel's bytes attains on this GPU."""
+    n = (nbytes + 15) // 16 * 16
+    nrot = max(2, math.ceil(ROTATE_BYTES / n))
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(nrot)]
+    sink = torch.empty((bn.lib().bitnet_probe_stream_read_sink_len(n),), dtype=torch.int32, device="cuda")
+    us = graph_us_per_launch(torch, lambda i: bn.bitnet_probe_stream_read(bufs[i % nrot], sink, 0), nrot, reps)
+    us_noout = graph_us_per_launch(torch, lambda i: bn.bitnet_probe_stream_read(bufs[i % nrot], sink, 1), nrot, reps)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"what": "one pass of 16-byte loads, one per thread, over the same number of bytes, each wave storing "
+                    "one word (bitnet_probe_stream_read mode 0); no_output: the same read storing nothing (mode 1)",
+            "bytes": n, "us": us, "GBps": n / us / 1e3, "no_output_us": us_noout, "no_output_GBps": n / us_noout / 1e3}
 
 
 def prefill_shape(torch, bn, wl, reps=10):
@@ -421,6 +440,8 @@ def main():
     pbytes = N * K // 4
     ab = gemv_bytes(M, N, K)
     achieved = ab / gemv_us / 1e3
+    attain = attainable_read(torch, bn, ab, reps)
+    attain["product_frac_of_attainable"] = achieved / attain["GBps"]
     result = {
         "metric": "W2A8 GEMV packed-weight GB/s, 13824x2560 batch 1 (quantise + product per step)",
         "value": pbytes / (ms_per_step * 1e-3) / 1e9,
@@ -446,11 +467,13 @@ def main():
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(), "alg_bytes_per_launch": ab, "kernel_us": gemv_us,
             "packed_GBps_kernel": pbytes / gemv_us / 1e3,
+            "attainable_read": attain,
         },
     }
     log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
         f"gemv {gemv_us:.2f} us, quant {quant_us:.2f} us, two-launch step {step2_us:.2f} us, "
-        f"eager step {eager_us:.2f} us")
+        f"eager step {eager_us:.2f} us; a bare read of the same {attain['bytes']} B takes {attain['us']:.2f} us "
+        f"({attain['GBps']:.0f} GB/s)")
     del d
     torch.cuda.empty_cache()
 

@@ -66,6 +66,9 @@ _SIGS = {
     "bitnet_w2a8_gemv": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_gemm": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_scale_count_g": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int], ctypes.c_size_t),
+    "bitnet_probe_stream_read_sink_len": ([ctypes.c_size_t], ctypes.c_size_t),
+    "bitnet_probe_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p], ctypes.c_int),
     "bitnet_ternarize_absmean_g": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p], ctypes.c_int),
     "bitnet_pack_i2s_g": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -476,3 +479,19 @@ class Chain:
                                     M, _dev_ptr(y, "y"), _dev_ptr(ws, "workspace"), ws.numel(), _stream(stream)),
             "bitnet_w2a8_chain")
         return y
+
+
+# ------------------------------------------------------------------ measurement helper
+def bitnet_probe_stream_read(src, sink=None, mode=0, stream=None):
+    """One plain pass of 16-byte loads over the device tensor `src` (not part of
+    the product path; the benchmark's attainable-bandwidth reference).  mode 0:
+    returns the uint32 sink whose sum (mod 2^32) is the sum of src's 32-bit
+    words; mode 1: no output (the read-only floor), the sink is left as it was."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    nsink = lib().bitnet_probe_stream_read_sink_len(nbytes)
+    if sink is None:
+        sink = torch.empty((nsink,), dtype=torch.int32, device=src.device)
+    _ok(lib().bitnet_probe_stream_read(_dev_ptr(src, "src"), nbytes, _dev_ptr(sink, "sink"), sink.numel(), int(mode),
+                                       _stream(stream)), "bitnet_probe_stream_read")
+    return sink

@@ -301,6 +301,23 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
 bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int32_t *acc,
                                     int M, int N, int K, hipStream_t stream);
 
+/* ---------------------------------------------------------------- measurement helper */
+
+/* Not part of the product path: one plain pass of 16-byte loads over `bytes`
+ * of device memory, the bandwidth a bare stream attains at that size, against
+ * which the benchmark prices the product kernels next to the published HBM
+ * peak.  mode 0: every wave writes the wrapping 32-bit sum of the words it
+ * read to one sink entry, so the sum of all entries (mod 2^32) is the sum of
+ * every 32-bit word of the buffer; mode 1: a wave writes only if its sum equals
+ * one fixed value (practically never) -- the floor of a read with no output,
+ * since a kernel completes only when its stores are acknowledged.
+ *   src   device, 16-byte aligned, bytes % 16 == 0 (else UNSUPPORTED_SHAPE)
+ *   sink  device, uint32 [sink_len], sink_len >= bitnet_probe_stream_read_sink_len(bytes)
+ *   mode  0 or 1 (else INVALID_ARG) */
+size_t bitnet_probe_stream_read_sink_len(size_t bytes);
+bitnet_status_t bitnet_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, size_t sink_len, int mode,
+                                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -348,3 +348,16 @@ def test_max_k_integer_sums_do_not_overflow(gpu):
     with pytest.raises(bn.BitnetError) as ei:
         bn.bitnet_w2a8_acc_i32(pb, dev(np.ones((M, K + 128), np.int8)), N, K + 128)
     assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+
+
+# ------------------------------------------------------------------ measurement helper
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 10_011_152])
+def test_stream_read_probe_reads_every_word(gpu, nbytes):
+    # the benchmark's bare-stream reference must really read the whole buffer once
+    words = wl.rng_for(98, nbytes).integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    sink = host(bn.bitnet_probe_stream_read(dev(words.view(np.int32))))
+    assert int(sink.view(np.uint32).astype(np.uint64).sum()) % 2 ** 32 == int(words.astype(np.uint64).sum()) % 2 ** 32
+    # mode 1 stores nothing unless a wave total hits the fixed value
+    marker = torch.full(sink.shape, 7, dtype=torch.int32, device="cuda")
+    after = host(bn.bitnet_probe_stream_read(dev(words.view(np.int32)), sink=marker, mode=1))
+    assert np.count_nonzero(after != 7) <= np.count_nonzero(sink.view(np.uint32) == 0x9E3779B9)
