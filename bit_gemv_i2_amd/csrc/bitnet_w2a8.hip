@@ -828,8 +828,278 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
 }
 
 // --------------------------------------------------------------------------
+// a6, 256-row form (the prefill shapes): same tiles, operands and arithmetic as
+// gemm_kernel<OUT, SG, 4>, so results are bit-identical to it, but the data
+// arrives and the work is ordered differently.
+//  * Each block's activations (128 x 128 int8), 16 bricks and 256 scales go
+//    straight from global memory into one of 4 LDS stages with
+//    global_load_lds (no staging registers, no LDS store instructions), three
+//    blocks ahead.  The activation tile is unpadded; chunk c of row r sits at
+//    position c ^ (r & 7), which keeps the operand reads conflict-free.
+//  * A SIMD runs one wave's VALU work in the shadow of that same wave's
+//    matrix-core steps (about two VALU operations per step come for free), but
+//    VALU work of one wave next to matrix-core work of another wave on the same
+//    SIMD runs slower than the two one after the other.  So every wave does the
+//    same thing at the same time and interleaves inside its own stream: a block
+//    is two halves of 16 steps (row tiles 0-1, then 2-3; K-step 0 of the 8
+//    tiles, then K-step 1), and after each step the wave drains half of one
+//    finished tile of the other pair into fp32 and decodes one dword of the
+//    weights the next half needs.  Half 0 drains the previous block's tiles
+//    2-3 and decodes this block's tiles 2-3; half 1 drains this block's tiles
+//    0-1 and decodes the next block's tiles 0-1.
+//  * bf16 results leave through LDS as whole 512-byte token rows.
+// The direct loads are issued from inline asm, so the compiler neither counts
+// them nor makes LDS reads wait for them: each wave waits for its own loads of
+// a stage (s_waitcnt vmcnt) before the barrier that publishes the stage.
+// --------------------------------------------------------------------------
+constexpr int kWideStages = 4;
+constexpr int kWideAStage = kGemmBM * kBlockK;  // 16384 bytes, unpadded, swizzled
+constexpr int kWideRowStride = 528;             // bf16 epilogue: 256 values + 16 bytes per token row
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the wave's
+// 1 KB slice); M0 carries the LDS address and is restored afterwards.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+
+// wait until at most N of this wave's global loads are pending and all its LDS
+// reads are done, then meet the workgroup
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int OUT, int SG>  // SG 128 or 0
+__global__ __launch_bounds__(kGemmThreads) void gemm_wide_kernel(const uint8_t *__restrict__ packed,
+                                                                  const float *__restrict__ scales,
+                                                                  const int8_t *__restrict__ q,
+                                                                  const float *__restrict__ s_a,
+                                                                  void *__restrict__ yout, int M, int N, int K,
+                                                                  int ntm) {
+    constexpr bool BLOCKED = OUT != 2 && SG != 0;
+    constexpr int S = kWideStages;
+    constexpr int STAGE = kWideAStage + kBStage + (BLOCKED ? kSStage : 0);
+    __shared__ __align__(16) unsigned char lds[S * STAGE];
+    static_assert(kGemmBM * kWideRowStride <= S * STAGE, "epilogue tile fits the stages");
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // LDS byte address (low half of the flat address)
+    const int G = gridDim.x;
+    int t = blockIdx.x;
+    if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // XCD-aware order
+    const int tm = t % ntm, tn = t / ntm;
+    const int m0 = tm * kGemmBM, T0 = tn * 16;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, g = l >> 4, j = l & 15;
+    const int wm = w >> 2, wn = w & 3;
+    const int nblk = K >> 7, ntile_n = N >> 4;
+
+    // Direct-load sources of this lane (block 0; each block adds a fixed step).
+    // Activations: wave w fills rows 16w..16w+15 with two 1 KB loads; lane l of
+    // load i lands on row 16w + 8i + l/8 at chunk position l%8, which holds
+    // logical chunk (l%8) ^ (l/8).  Rows past M repeat row 0 (never stored).
+    const int8_t *asrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * w + 8 * i + (l >> 3);
+        const int tok = m0 + r < M ? m0 + r : 0;
+        asrc[i] = q + (size_t)tok * K + (((l & 7) ^ (l >> 3)) * 16);
+    }
+    // Bricks: wave w fills bricks 2w, 2w+1 (512 B each) with one 1 KB load.
+    const int bT = min(T0 + 2 * w + (l >> 5), ntile_n - 1);
+    const uint8_t *bsrc = packed + (size_t)bT * nblk * kBrickBytes + (l & 31) * 16;
+    // Scales: wave w fills tiles 2w, 2w+1 (64 B each) with lanes 0..7.
+    const int sT = min(T0 + 2 * w + (l >> 2), ntile_n - 1);
+    const float *ssrc = BLOCKED ? scales + (size_t)sT * nblk * kTileN + (l & 3) * 4 : nullptr;
+
+    auto issue = [&](int b) {  // this wave's loads of block b (clamped) into stage b % S
+        const int bb = min(b, nblk - 1);
+        const uint32_t st = lds0 + (uint32_t)((b % S) * STAGE);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(asrc[i] + (size_t)bb * kBlockK, st + (2 * w + i) * 1024);
+        dma16(bsrc + (size_t)bb * kBrickBytes, st + kWideAStage + w * 1024);
+        if (BLOCKED && l < 8) dma16(ssrc + (size_t)bb * kTileN, st + kWideAStage + kBStage + w * 128);
+    };
+    constexpr int kLoadsPerBlock = BLOCKED ? 4 : 3;  // per wave (the scale load with 8 lanes)
+
+    float yacc[4][4][4];
+    v4i c[4][4];
+    float sc[4][4];  // block scales of rows 4g..4g+3 of the wave's row tiles
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            c[a][b] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[a][b][e] = 0.0f, sc[a][e] = 0.0f;
+        }
+    v4i ao[4][2], bw[4][2];  // activation operands [token tile][K-step], decoded weights [row tile][K-step]
+    uint32_t wr[4][2];        // packed weight words [row tile][K-step]
+
+    auto sbase = [&](int b) { return lds + (b % S) * STAGE; };
+    auto read_ao = [&](int b, int s) {
+        const unsigned char *base = sbase(b);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const int r = 64 * wm + 16 * ti + j;
+            ao[ti][s] = *reinterpret_cast<const v4i *>(base + r * kBlockK + (((4 * s + g) ^ (r & 7)) * 16));
+        }
+    };
+    auto read_wr = [&](int b, int tj0) {  // row tiles tj0, tj0 + 1
+        const unsigned char *base = sbase(b);
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(base + kWideAStage + (4 * wn + tj0 + d) * 512 + l * 8);
+            wr[tj0 + d][0] = v.x;
+            wr[tj0 + d][1] = v.y;
+        }
+    };
+    auto read_sc = [&](int b, int tj0) {  // row tiles tj0, tj0 + 1
+        if constexpr (BLOCKED) {
+            const unsigned char *base = sbase(b);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(base + kWideAStage + kBStage +
+                                                                    ((4 * wn + tj0 + d) * 16 + 4 * g) * 4);
+                sc[tj0 + d][0] = s4.x;
+                sc[tj0 + d][1] = s4.y;
+                sc[tj0 + d][2] = s4.z;
+                sc[tj0 + d][3] = s4.w;
+            }
+        }
+    };
+    // Half h: 16 steps on row tiles 2h, 2h+1.  After step k: elements 2(k&1), 2(k&1)+1 of
+    // tile (k/4, o + (k/2 & 1)) of the other pair o are drained (the order those tiles
+    // finished in), and dword k&3 of K-step (k/4 & 1) of row tile dt0 + k/8 is decoded
+    // (the shifts of decode16).  Half 1 reloads K-step 0's activations for block bnext
+    // once its own K-step-0 steps are done.
+    auto half = [&](int h, int dt0, int bnext) {
+        const int o = 2 - 2 * h;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int s = k >> 3, ti = (k >> 1) & 3, tj = 2 * h + (k & 1);
+            c[ti][tj] = mfma_i8(bw[tj][s], ao[ti][s], (BLOCKED && s == 0) ? v4i{0, 0, 0, 0} : c[ti][tj]);
+            if constexpr (BLOCKED) {
+                const int dti = k >> 2, dtj = o + ((k >> 1) & 1), e0 = 2 * (k & 1);
+#pragma unroll
+                for (int e = e0; e < e0 + 2; ++e)
+                    yacc[dti][dtj][e] = fmaf(sc[dtj][e], (float)c[dti][dtj][e], yacc[dti][dtj][e]);
+            }
+            {
+                const int dtj = dt0 + (k >> 3), ds = (k >> 2) & 1, p = k & 3;
+                bw[dtj][ds][p] = (int)((wr[dtj][ds] << (6 - 2 * p)) & 0xC0C0C0C0u);
+            }
+            if (h == 1 && k == 7) read_ao(bnext, 0);
+        }
+    };
+
+    // Prologue: blocks 0..2 in flight, 0 and 1 complete and published.
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_loads_barrier<kLoadsPerBlock>();
+    read_ao(0, 0);
+    read_wr(0, 0);
+    read_wr(0, 2);
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+        bw[tj][0] = decode16(wr[tj][0]);
+        bw[tj][1] = decode16(wr[tj][1]);
+    }
+    // Block b reads stage b (K-step 1 activations, scales) and stage b+1 (weights and K-step 0
+    // activations of the next block).  The barrier at its top publishes block b+1: every wave
+    // has finished its own loads of it, only block b+2 may still be pending.  Block b+3 then
+    // refills the stage of block b-1, which nobody reads after that barrier.  The first
+    // half-0 drains zeros (c and sc start at 0).
+    for (int b = 0; b < nblk; ++b) {
+        if (b > 0) wait_loads_barrier<kLoadsPerBlock>();
+        issue(b + 3);
+        read_ao(b, 1);
+        read_sc(b, 0);
+        half(0, 2, b + 1);
+        read_wr(b + 1, 0);
+        read_sc(b, 2);
+        half(1, 0, b + 1);
+        read_wr(b + 1, 2);
+    }
+    if constexpr (BLOCKED) {  // the last block's tiles 2-3
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 2; tj < 4; ++tj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) yacc[ti][tj][e] = fmaf(sc[tj][e], (float)c[ti][tj][e], yacc[ti][tj][e]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped tail loads still in flight
+
+    // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j, row
+    // 16(T0+4wn+tj)+4g+e
+    if constexpr (OUT == 0) {  // bf16 through LDS: each store instruction writes two whole token rows
+        wait_loads_barrier<0>();  // every wave past its last stage read
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const int r = 64 * wm + 16 * ti + j;
+            const int m = m0 + r;
+            const float f = m < M ? (BLOCKED ? s_a[m] * 0.015625f : s_a[m] * scales[0]) : 0.0f;
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = BLOCKED ? yacc[ti][tj][e] : (float)(c[ti][tj][e] >> 6);
+                const uint32_t lo = f32_to_bf16_rne(v[0] * f) | ((uint32_t)f32_to_bf16_rne(v[1] * f) << 16);
+                const uint32_t hi = f32_to_bf16_rne(v[2] * f) | ((uint32_t)f32_to_bf16_rne(v[3] * f) << 16);
+                *reinterpret_cast<uint2 *>(lds + r * kWideRowStride + ((4 * wn + tj) * 16 + 4 * g) * 2) =
+                    make_uint2(lo, hi);
+            }
+        }
+        wait_loads_barrier<0>();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * w + 2 * i + (l >> 5);
+            const int m = m0 + r;
+            const int col = T0 * 16 + (l & 31) * 8;
+            if (m < M && col < N)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(yout) + (size_t)m * N + col) =
+                    *reinterpret_cast<const uint4 *>(lds + r * kWideRowStride + (l & 31) * 16);
+        }
+    } else {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const int m = m0 + 64 * wm + 16 * ti + j;
+            if (m >= M) continue;
+            const float f = (OUT == 2) ? 0.0f : BLOCKED ? s_a[m] * 0.015625f : s_a[m] * scales[0];
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                const int T = T0 + 4 * wn + tj;
+                if (T >= ntile_n) continue;
+                const size_t idx = (size_t)m * N + (size_t)T * 16 + 4 * g;
+                if (OUT == 1) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = BLOCKED ? yacc[ti][tj][e] : (float)(c[ti][tj][e] >> 6);
+                    *reinterpret_cast<float4 *>(static_cast<float *>(yout) + idx) =
+                        make_float4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                } else {
+                    *reinterpret_cast<int4 *>(static_cast<int32_t *>(yout) + idx) =
+                        make_int4(c[ti][tj][0] >> 6, c[ti][tj][1] >> 6, c[ti][tj][2] >> 6, c[ti][tj][3] >> 6);
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
 // host-side launch helpers
 // --------------------------------------------------------------------------
+
 bool shape_ok(int64_t N, int64_t K) { return bitnet_check_shape(N, K) == BITNET_OK; }
 
 bitnet_status_t launched() {
@@ -983,7 +1253,12 @@ void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float 
     const int ntm = (M + kGemmBM - 1) / kGemmBM, rt = gemm_row_tiles(M, N);
     const int ntn = (N + 64 * rt - 1) / (64 * rt);
     const dim3 grid(ntm * ntn), block(kGemmThreads);
-    if (rt == 4) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 4>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    if (rt == 4) {
+        if constexpr (SG != 64)  // direct staging, in-wave interleaving
+            hipLaunchKernelGGL((gemm_wide_kernel<OUT, SG>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        else
+            hipLaunchKernelGGL((gemm_kernel<OUT, SG, 4>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    }
     else if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
     else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
 }
