@@ -998,6 +998,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_wide_kernel(const uint8_t *
                 bw[dtj][ds][p] = (int)((wr[dtj][ds] << (6 - 2 * p)) & 0xC0C0C0C0u);
             }
             if (h == 1 && k == 7) read_ao(bnext, 0);
+            // unscaled: keep the written order (the compiler otherwise hoists K-step 1 steps
+            // up to their just-issued operand reads and stalls on them)
+            if constexpr (!BLOCKED) __builtin_amdgcn_sched_barrier(0);
         }
     };
 
