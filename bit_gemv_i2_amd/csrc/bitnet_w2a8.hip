@@ -358,11 +358,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
 
     // vmcnt retires loads in issue order: whatever is needed before the
     // weights arrive (activations to quantise or stage) is issued before them.
-    float sa_pre[NE];
-    if (!FUSED && !INT_OUT) {
-#pragma unroll
-        for (int e = 0; e < NE; ++e) sa_pre[e] = args.s_a[min(4 * g + e, M - 1)];
-    }
+    // token scale of the output this lane stores (token l/4, see the epilogue)
+    const float sa_tok = (!FUSED && !INT_OUT) ? args.s_a[min(l >> 2, M - 1)] : 0.0f;
     const float s_w = (SG == 0 && !INT_OUT) ? args.scales[0] : 0.0f;  // the one weight scale
     // kAllWaves: this wave's K-slice of every token, raw, 8 values per chunk
     constexpr int CR = (NB + 3) / 4;
@@ -523,29 +520,52 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     for (int e = 0; e < NE; ++e) red[(w * 4 + e) * kWave + l] = IACC ? iacc[e] : __float_as_int(yacc[e]);
     if (LDSQ) lds_barrier();
     else __syncthreads();
-    if (w == 0) {
-        const int n = tile * kTileN + j;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            const int m = 4 * g + e;
-            if (INT_OUT) {
+    // Wave 0 sums the waves' partials (in wave order) and stores.  One token: lanes
+    // 0..15 each store row j.  More tokens: lane l takes token mt = l/4 and rows
+    // 4(l%4)..4(l%4)+3 of the tile (element mt%4 of lanes 16(mt/4) + r), so each stored
+    // token row leaves as 16-byte pieces, one store instruction per workgroup (four
+    // 4-byte stores per lane cost ~0.8 us more at 8 tokens; for one token the 16-lane
+    // form is ~0.1 us faster).
+    if (TOK == 1 && w == 0) {
+        if (g == 0) {
+            const size_t o = (size_t)tile * kTileN + j;
+            if (INT_OUT || SG == 0) {
                 int sum = 0;
-                for (int ww = 0; ww < nwc; ++ww) sum += red[(ww * 4 + e) * kWave + l];
-                if (m < M) args.acc[(size_t)m * N + n] = sum >> 6;  // exact: sum is 64 * integer
-            } else if (SG == 0) {  // exact integer product, then the two scales
-                int sum = 0;
-                for (int ww = 0; ww < nwc; ++ww) sum += red[(ww * 4 + e) * kWave + l];
-                if (m < M) {
-                    const float sa = FUSED ? tail[m] : sa_pre[e];
-                    args.y[(size_t)m * N + n] = (float)(sum >> 6) * (sa * s_w);
-                }
+                for (int ww = 0; ww < nwc; ++ww) sum += red[ww * 4 * kWave + l];
+                if (INT_OUT) args.acc[o] = sum >> 6;  // exact: sum is 64 * integer
+                else args.y[o] = (float)(sum >> 6) * ((FUSED ? tail[0] : sa_tok) * s_w);
             } else {
                 float sum = 0.0f;
-                for (int ww = 0; ww < nwc; ++ww) sum += __int_as_float(red[(ww * 4 + e) * kWave + l]);
-                if (m < M) {
-                    const float sa = FUSED ? tail[m] : sa_pre[e];
-                    args.y[(size_t)m * N + n] = sum * (sa * 0.015625f);
+                for (int ww = 0; ww < nwc; ++ww) sum += __int_as_float(red[ww * 4 * kWave + l]);
+                args.y[o] = sum * ((FUSED ? tail[0] : sa_tok) * 0.015625f);
+            }
+        }
+    } else if (w == 0) {
+        const int mt = l >> 2, r4 = (l & 3) * 4;
+        const int src = (mt & 3) * kWave + 16 * (mt >> 2) + r4;
+        if (mt < M) {
+            const size_t o = (size_t)mt * N + (size_t)tile * kTileN + r4;
+            if (INT_OUT || SG == 0) {
+                int sum[4] = {0, 0, 0, 0};
+                for (int ww = 0; ww < nwc; ++ww)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sum[r] += red[ww * 4 * kWave + src + r];
+                if (INT_OUT) {  // exact: each sum is 64 * integer
+                    *reinterpret_cast<int4 *>(args.acc + o) =
+                        make_int4(sum[0] >> 6, sum[1] >> 6, sum[2] >> 6, sum[3] >> 6);
+                } else {  // exact integer product, then the two scales
+                    const float f = (FUSED ? tail[mt] : sa_tok) * s_w;
+                    *reinterpret_cast<float4 *>(args.y + o) =
+                        make_float4((float)(sum[0] >> 6) * f, (float)(sum[1] >> 6) * f, (float)(sum[2] >> 6) * f,
+                                    (float)(sum[3] >> 6) * f);
                 }
+            } else {
+                float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int ww = 0; ww < nwc; ++ww)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sum[r] += __int_as_float(red[ww * 4 * kWave + src + r]);
+                const float f = (FUSED ? tail[mt] : sa_tok) * 0.015625f;
+                *reinterpret_cast<float4 *>(args.y + o) = make_float4(sum[0] * f, sum[1] * f, sum[2] * f, sum[3] * f);
             }
         }
     }
@@ -1318,7 +1338,7 @@ bitnet_status_t bitnet_quant_act_relu2_glu(const float *y, int M, int H, int8_t 
 bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q, const float *s_a,
                                  float *y, int M, int N, int K, hipStream_t stream) {
     if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
-    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 4))
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     GemvArgs a{packed, scales, q, s_a, y, nullptr, nullptr, nullptr, M, N, K, 0, 0, 0};
@@ -1343,7 +1363,7 @@ bitnet_status_t bitnet_w2a8_gemv_g(const uint8_t *packed, const float *scales, c
     if (scale_block == 128) return bitnet_w2a8_gemv(packed, scales, q, s_a, y, M, N, K, stream);
     if (scale_block != 64 && scale_block != 0) return BITNET_ERR_INVALID_ARG;
     if (!packed || !scales || !q || !s_a || !y) return BITNET_ERR_INVALID_ARG;
-    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 4))
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (scale_block == 0 && K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
@@ -1377,7 +1397,7 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
                                      float *y, int8_t *q_out, float *s_a_out, int M, int N, int K,
                                      hipStream_t stream) {
     if (!packed || !scales || !x || !y) return BITNET_ERR_INVALID_ARG;
-    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(x, 16) || !aligned(y, 4) ||
+    if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(x, 16) || !aligned(y, 16) ||
         !aligned(q_out, 16) || !aligned(s_a_out, 4))
         return BITNET_ERR_INVALID_ARG;
     if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32 && xdt != BITNET_DT_F32_FOLD2 &&
@@ -1460,7 +1480,7 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
 
 bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
                                   float *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!x || !y || !workspace || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 256))
+    if (!x || !y || !workspace || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
         return BITNET_ERR_INVALID_ARG;
     if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
     if (!layers || n < 1) return BITNET_ERR_INVALID_ARG;

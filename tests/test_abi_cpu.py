@@ -142,6 +142,17 @@ def test_gemv_validation(M, N, K, ptr, want):
     assert st == want
 
 
+def test_decode_outputs_must_be_16_byte_aligned():
+    # the decode kernels store each token's four consecutive rows as one 16-byte piece
+    L = bn.lib()
+    assert L.bitnet_w2a8_gemv(_FAKE, _FAKE, _FAKE, _FAKE, _MIS, 8, 2560, 2560, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_gemv_g(_FAKE, _FAKE, _FAKE, _FAKE, _MIS, 8, 2560, 2560, 0, _NULL) == \
+        bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_gemv_act(_FAKE, _FAKE, _FAKE, 0, _MIS, _NULL, _NULL, 1, 2560, 2560, _NULL) == \
+        bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_acc_i32(_FAKE, _FAKE, _MIS, 8, 2560, 2560, _NULL) == bn.BITNET_ERR_INVALID_ARG
+
+
 def test_gemm_acc_quant_validation():
     L = bn.lib()
     assert L.bitnet_w2a8_gemm(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 7, 4, 16, 128, _NULL) == bn.BITNET_ERR_INVALID_ARG
