@@ -325,6 +325,61 @@ def test_gemm_row_tile_choices_sampled(gpu, M, N, K):
     assert np.isfinite(y32).all()
 
 
+# ------------------------------------------------------------------ the 256-row form on ragged shapes
+# A launch with at least 200 workgroups of 128 tokens x 256 rows runs the 256-row kernel
+# (weights and activations loaded straight into a ring of four LDS stages, matrix-core
+# steps interleaved with the drain).  These shapes reach it with a partial last token tile,
+# a partial last 256-row group (clamped weight loads, stores cut at N) and 1, 2, 3 and 5
+# K-blocks (with one block every prefetch repeats block 0; at five the ring wraps).
+def wide_form(M, N):
+    return -(-M // 128) * -(-N // 256) >= 200
+
+
+def edge_samples(r, M, N):
+    toks = {0, M - 1, (M // 128) * 128 % M} | set(r.choice(M, 10, replace=False).tolist())
+    tiles = {0, N // 16 - 1, (N // 256) * 16 % (N // 16)} | set(r.choice(N // 16, 12, replace=False).tolist())
+    toks, tiles = np.array(sorted(toks)), np.array(sorted(tiles))
+    return toks, (tiles[:, None] * 16 + np.arange(16)).ravel()
+
+
+@pytest.mark.parametrize("M,N,K", [(3207, 2064, 384), (1700, 4112, 128), (2000, 3328, 640), (1000, 6400, 256)])
+def test_gemm_wide_form_ragged_sampled(gpu, M, N, K):
+    assert wide_form(M, N)
+    c = wl.small_case(M + N + K, M, N, K)
+    p, st = pack_dev(c.T, c.S)
+    qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    yb = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, N, K, y=torch.full((M, N), float("nan"), dtype=torch.bfloat16,
+                                                                    device="cuda")).view(torch.int16)).view(np.uint16)
+    y32 = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, N, K,
+                                   y=torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")))
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, N, K))
+    toks, rows = edge_samples(wl.rng_for(98, M, N, K), M, N)
+    ref = oracle.w2a8(oracle.pack_i2s(c.T[rows]), c.S[rows], qo[toks], so[toks], rows.size, K)
+    assert np.array_equal(acc[np.ix_(toks, rows)], ref["acc"])
+    assert_f32_close(y32[np.ix_(toks, rows)], ref, f"wide f32 {M}x{N}x{K}")
+    assert_bf16_ok(yb[np.ix_(toks, rows)], ref, f"wide bf16 {M}x{N}x{K}")
+    # every output element is written (both buffers started as NaN)
+    assert np.isfinite(y32).all() and np.isfinite(wl.bf16_to_f32(yb)).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(3207, 2064, 384), (1700, 4112, 128)])
+def test_gemm_wide_form_one_scale_ragged_sampled(gpu, M, N, K):
+    assert wide_form(M, N)
+    c = wl.small_case(M + N + K + 1, M, N, K)
+    S0 = np.array([0.75], np.float32)
+    p, st = bn.bitnet_pack_i2s_g(c.T, S0, 0)
+    p, st = dev(p), dev(st)
+    qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    y32 = host(bn.bitnet_w2a8_gemm_g(p, st, qd, sd, N, K, 0, out_dtype=torch.float32))
+    yb = host(bn.bitnet_w2a8_gemm_g(p, st, qd, sd, N, K, 0).view(torch.int16)).view(np.uint16)
+    toks, rows = edge_samples(wl.rng_for(99, M, N, K), M, N)
+    ref = oracle.w2a8_g(oracle.pack_i2s_g(c.T[rows], 0), S0, qo[toks], so[toks], rows.size, K, 0)
+    assert_f32_close(y32[np.ix_(toks, rows)], ref, f"wide G=0 f32 {M}x{N}x{K}")
+    assert_bf16_ok(yb[np.ix_(toks, rows)], ref, f"wide G=0 bf16 {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ the largest K
 def test_max_k_integer_sums_do_not_overflow(gpu):
     # the int32 accumulators hold 64 x the integer sum: at the largest K with every
