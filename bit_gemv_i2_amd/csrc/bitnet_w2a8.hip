@@ -321,7 +321,8 @@ enum GemvForm {
     kMulti = 1,     // as kDirect with a loop over chunks (K beyond 12 x 8 blocks)
     kStaged = 2,    // int8 q slice fetched with a few coalesced loads into LDS (M <= 4)
     kAllWaves = 3,  // fused quantisation, every compute wave quantises its own K-slice (M <= 4)
-    kQuantWaves = 4 // fused quantisation by 4 extra quant waves (4 < M <= 16)
+    kQuantWaves = 4, // fused quantisation by 4 extra quant waves (4 < M <= 16)
+    kAllWavesXF = 5  // as kAllWaves, quantising before the weights are requested (bf16 activations)
 };
 
 template <int AM, int NB, int TOK, bool INT_OUT, int FORM, int SG>
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
     constexpr int NE = INT_OUT ? 4 : MW;
     constexpr bool FUSED = AM >= 0;
-    constexpr bool LDSQ = FORM == kStaged || FORM == kAllWaves || FORM == kQuantWaves;  // operands via LDS
+    constexpr bool ALLW = FORM == kAllWaves || FORM == kAllWavesXF;  // every wave quantises its slice
+    constexpr bool LDSQ = FORM == kStaged || ALLW || FORM == kQuantWaves;  // operands via LDS
     constexpr int XM = AM < 0 ? 0 : AM;
     int *red = reinterpret_cast<int *>(smem);
     int8_t *qs = reinterpret_cast<int8_t *>(smem);
@@ -363,13 +365,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     const float s_w = (SG == 0 && !INT_OUT) ? args.scales[0] : 0.0f;  // the one weight scale
     // kAllWaves: this wave's K-slice of every token, raw, 8 values per chunk
     constexpr int CR = (NB + 3) / 4;
-    Raw8<XM> xr[FORM == kAllWaves ? MW : 1][FORM == kAllWaves ? CR : 1];
+    Raw8<XM> xr[ALLW ? MW : 1][ALLW ? CR : 1];
     const int nchw = nbw * 16;
-    if (FORM == kAllWaves) {
+    if (ALLW) {
 #pragma unroll
-        for (int m = 0; m < (FORM == kAllWaves ? MW : 1); ++m)
+        for (int m = 0; m < (ALLW ? MW : 1); ++m)
 #pragma unroll
-            for (int r = 0; r < (FORM == kAllWaves ? CR : 1); ++r)
+            for (int r = 0; r < (ALLW ? CR : 1); ++r)
                 xr[m][r] = load_raw8<XM>(args.act, min(m, M - 1), K, bw0 * 16 + min(l + kWave * r, nchw - 1));
     }
     // kStaged: this wave's K-slice of q for M <= TOK tokens in 16-byte chunks
@@ -404,69 +406,91 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
         const float *sp = args.scales + (((size_t)tile * nblk + c0) * kTileN + j) * (SG == 64 ? 2 : 1);
         uint2 wv[NB];
         float2 sc[NB];
+        auto load_weights = [&]() {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {  // unconditional (clamped) loads, issued back to back
-            const int bi = min(i, nb - 1);
-            wv[i] = *reinterpret_cast<const uint2 *>(wp + bi * kBrickBytes);
-            if (!INT_OUT && SG == 128) sc[i].x = sp[bi * kTileN];
-            if (!INT_OUT && SG == 64) sc[i] = *reinterpret_cast<const float2 *>(sp + bi * 2 * kTileN);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FORM == kStaged) {
+            for (int i = 0; i < NB; ++i) {  // unconditional (clamped) loads, issued back to back
+                const int bi = min(i, nb - 1);
+                wv[i] = *reinterpret_cast<const uint2 *>(wp + bi * kBrickBytes);
+                if (!INT_OUT && SG == 128) sc[i].x = sp[bi * kTileN];
+                if (!INT_OUT && SG == 64) sc[i] = *reinterpret_cast<const float2 *>(sp + bi * 2 * kTileN);
+            }
+        };
+        if constexpr (ALLW) {
+            // each wave quantises its own K-slice of every token; one LDS exchange gives the
+            // per-token amax.  No barrier after: each wave reads back only the slice it wrote.
+            auto quantise_slices = [&]() {
+                float *amax_part = tail + 16;
+                float xf[MW][CR][8];
 #pragma unroll
-            for (int r = 0; r < QR; ++r) {
-                const int c = l + kWave * r;
-                if (c < M * qper) {
-                    const int m = c / qper, o = c - m * qper;
-                    *reinterpret_cast<v4i *>(qs + (size_t)m * lds_qstride(K) + (size_t)bw0 * kBlockK + 16 * o) = qraw[r];
+                for (int m = 0; m < MW; ++m)
+#pragma unroll
+                    for (int r = 0; r < CR; ++r) cvt8<XM>(xr[m][r], xf[m][r]);
+#pragma unroll
+                for (int m = 0; m < MW; ++m) {
+                    float mx = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < CR; ++r)
+                        if (l + kWave * r < nchw) mx = max_abs8(xf[m][r], mx);
+                    mx = wave_max(mx);
+                    if (l == 0) amax_part[w * 4 + m] = mx;
                 }
-            }
-            // the wave reads back only its own slice: LDS keeps one wave's accesses in order
-        } else if constexpr (FORM == kAllWaves) {
-            float *amax_part = tail + 16;
-            float xf[MW][CR][8];
+                lds_barrier();
 #pragma unroll
-            for (int m = 0; m < MW; ++m)
+                for (int m = 0; m < MW; ++m) {
+                    if (m >= M) break;
+                    float am = 0.0f;
+                    for (int ww = 0; ww < nwc; ++ww) am = fmaxf(am, amax_part[ww * 4 + m]);
+                    const float amax_c = fmaxf(am, 1e-5f);
+                    const float inv = __fdiv_rn(127.0f, amax_c);
 #pragma unroll
-                for (int r = 0; r < CR; ++r) cvt8<XM>(xr[m][r], xf[m][r]);
-#pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                float mx = 0.0f;
-#pragma unroll
-                for (int r = 0; r < CR; ++r)
-                    if (l + kWave * r < nchw) mx = max_abs8(xf[m][r], mx);
-                mx = wave_max(mx);
-                if (l == 0) amax_part[w * 4 + m] = mx;
-            }
-            lds_barrier();
-#pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                if (m >= M) break;
-                float am = 0.0f;
-                for (int ww = 0; ww < nwc; ++ww) am = fmaxf(am, amax_part[ww * 4 + m]);
-                const float amax_c = fmaxf(am, 1e-5f);
-                const float inv = __fdiv_rn(127.0f, amax_c);
-#pragma unroll
-                for (int r = 0; r < CR; ++r) {
-                    const int c = l + kWave * r;
-                    if (c < nchw) {
-                        const uint2 qv = quantize8(xf[m][r], inv);
-                        const size_t off = (size_t)bw0 * kBlockK + 8 * c;
-                        *reinterpret_cast<uint2 *>(qs + (size_t)m * lds_qstride(K) + off) = qv;
-                        if (args.q_out && blockIdx.x == 0)
-                            *reinterpret_cast<uint2 *>(args.q_out + (size_t)m * K + off) = qv;
+                    for (int r = 0; r < CR; ++r) {
+                        const int c = l + kWave * r;
+                        if (c < nchw) {
+                            const uint2 qv = quantize8(xf[m][r], inv);
+                            const size_t off = (size_t)bw0 * kBlockK + 8 * c;
+                            *reinterpret_cast<uint2 *>(qs + (size_t)m * lds_qstride(K) + off) = qv;
+                            if (args.q_out && blockIdx.x == 0)
+                                *reinterpret_cast<uint2 *>(args.q_out + (size_t)m * K + off) = qv;
+                        }
+                    }
+                    if (w == 0 && l == 0) {
+                        const float sa = __fdiv_rn(amax_c, 127.0f);
+                        tail[m] = sa;
+                        if (args.s_a_out && blockIdx.x == 0) args.s_a_out[m] = sa;
                     }
                 }
-                if (w == 0 && l == 0) {
-                    const float sa = __fdiv_rn(amax_c, 127.0f);
-                    tail[m] = sa;
-                    if (args.s_a_out && blockIdx.x == 0) args.s_a_out[m] = sa;
-                }
+            };
+            // The activations were requested before the weights.  When several workgroups
+            // share each CU and all fit at once, the weight requests of the whole grid delay
+            // that small read and the quantisation lands behind the weight stream; there
+            // (kAllWavesXF) the wave quantises first and requests its weights after.
+            if constexpr (FORM == kAllWavesXF) {
+                quantise_slices();
+                __builtin_amdgcn_sched_barrier(0);
+                load_weights();
+            } else {
+                load_weights();
+                __builtin_amdgcn_sched_barrier(0);
+                quantise_slices();
             }
-            // no barrier: each wave reads back only the slice it wrote itself
-        } else if constexpr (FORM == kQuantWaves) {
-            lds_barrier();  // q ready (written by the quant waves)
+        } else {
+            load_weights();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (FORM == kStaged) {
+#pragma unroll
+                for (int r = 0; r < QR; ++r) {
+                    const int c = l + kWave * r;
+                    if (c < M * qper) {
+                        const int m = c / qper, o = c - m * qper;
+                        *reinterpret_cast<v4i *>(qs + (size_t)m * lds_qstride(K) + (size_t)bw0 * kBlockK + 16 * o) = qraw[r];
+                    }
+                }
+                // the wave reads back only its own slice: LDS keeps one wave's accesses in order
+            } else if constexpr (FORM == kQuantWaves) {
+                lds_barrier();  // q ready (written by the quant waves)
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
         const int8_t *qp = qsrc + (size_t)j * (LDSQ ? lds_qstride(K) : K) + (size_t)c0 * kBlockK + g * 16;
         v4i a[NB][2];
 #pragma unroll
@@ -1140,7 +1164,7 @@ __host__ __device__ constexpr bool allwaves_fits(int xm, int tok, int nb) {
 // matrix); the fused forms exist for SG 128 only.
 template <int AM, int NB, bool INT_OUT, int FORM, int SG>
 void gemv_launch_tok(int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
-    if constexpr (FORM == kAllWaves) {  // M <= 4 and allwaves_fits (checked by the caller)
+    if constexpr (FORM == kAllWaves || FORM == kAllWavesXF) {  // M <= 4 and allwaves_fits (checked by the caller)
         if (tok == 1) hipLaunchKernelGGL((gemv_kernel<AM, NB, 1, false, FORM, 128>), grid, block, lds, st, a);
         else if (tok == 2) hipLaunchKernelGGL((gemv_kernel<AM, NB, 2, false, FORM, 128>), grid, block, lds, st, a);
         else if constexpr (allwaves_fits(AM < 0 ? 0 : AM, 4, NB))
@@ -1161,8 +1185,13 @@ void gemv_launch_tok(int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st,
 template <int AM, int NB, bool INT_OUT, int SG>
 void gemv_launch_form(int form, int tok, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvArgs &a) {
     if constexpr (AM >= 0) {
-        if (form == kQuantWaves) gemv_launch_tok<AM, NB, false, kQuantWaves, 128>(tok, grid, block, lds, st, a);
-        else gemv_launch_tok<AM, NB, false, kAllWaves, 128>(tok, grid, block, lds, st, a);
+        if (form == kQuantWaves) {
+            gemv_launch_tok<AM, NB, false, kQuantWaves, 128>(tok, grid, block, lds, st, a);
+        } else if (form == kAllWavesXF) {
+            if constexpr (AM == 0) gemv_launch_tok<AM, NB, false, kAllWavesXF, 128>(tok, grid, block, lds, st, a);
+        } else {
+            gemv_launch_tok<AM, NB, false, kAllWaves, 128>(tok, grid, block, lds, st, a);
+        }
     } else {
         if (form == kStaged) gemv_launch_tok<AM, NB, INT_OUT, kStaged, SG>(tok, grid, block, lds, st, a);
         else if (NB == 8 && form == kMulti) gemv_launch_tok<AM, 8, INT_OUT, kMulti, SG>(tok, grid, block, lds, st, a);
@@ -1233,6 +1262,20 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
         } else {
             form = kDirect;
             lds = (size_t)nw * 4 * kWave * sizeof(int);
+        }
+    }
+    // Fused all-waves form, bf16 activations: quantise before requesting the weights
+    // (kAllWavesXF) when the grid has more 16-row workgroups than CUs and all of them are
+    // resident at once (measured over
+    // 2560..20480 rows x K 2560..4096: 0.1-0.55 us faster there; with at most one workgroup
+    // per CU, or more waves than fit, the serial start costs 0.2-0.45 us instead).
+    if (AM == 0 && form == kAllWaves) {
+        int dev = 0, ncu = 0, thr = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipDeviceGetAttribute(&thr, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess) {
+            const int64_t wgs = a.N / kTileN, waves = wgs * (nw + a.qw);
+            if (wgs > ncu && waves <= (int64_t)ncu * (thr / kWave)) form = kAllWavesXF;
         }
     }
     const int nb = per < 8 ? per : 8;

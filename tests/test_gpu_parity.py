@@ -222,6 +222,25 @@ def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
     assert_f32_close(yh, oracle_ref(c.T, c.S, qo, so), f"gemv_act {mode} {M}x{N}x{K}")
 
 
+# With more 16-row workgroups than CUs (all resident), bf16 activations take the form that
+# quantises before requesting the weights; same arithmetic, so bit-identical to the unfused path.
+@pytest.mark.parametrize("M,N,K", [(1, 4112, 384), (2, 6912, 2560), (1, 13824, 2560), (4, 9216, 1280)])
+def test_gemv_act_quantise_first_form_bitexact(gpu, M, N, K):
+    assert N // 16 > torch.cuda.get_device_properties(0).multi_processor_count
+    c = wl.small_case(M * 7 + N + K, M, N, K, xkind="t3")
+    p, st = pack_dev(c.T, c.S)
+    xd = x_dev(c.x_bits)
+    qo, so = oracle.quant_act_bf16(c.x_bits)
+    qd, sd = bn.bitnet_quant_act(xd)
+    q_out = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_out = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = host(bn.bitnet_w2a8_gemv_act(p, st, xd, N, K, q_out=q_out, s_a_out=s_out))
+    y_ref = host(bn.bitnet_w2a8_gemv(p, st, qd, sd, N, K))
+    assert np.array_equal(host(q_out), qo) and np.array_equal(host(s_out), so)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32)), "fused and unfused differ"
+    assert_f32_close(y, oracle_ref(c.T, c.S, qo, so), f"gemv_act quantise-first {M}x{N}x{K}")
+
+
 def test_gemv_act_rejects_what_does_not_fit(gpu):
     # M*K beyond the LDS copy of q, and K beyond 12 waves x 8 blocks
     for (M, K) in [(16, 8192), (1, 12288 + 128)]:
