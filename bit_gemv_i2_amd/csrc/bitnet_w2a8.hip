@@ -322,7 +322,7 @@ enum GemvForm {
     kStaged = 2,    // int8 q slice fetched with a few coalesced loads into LDS (M <= 4)
     kAllWaves = 3,  // fused quantisation, every compute wave quantises its own K-slice (M <= 4)
     kQuantWaves = 4, // fused quantisation by 4 extra quant waves (4 < M <= 16)
-    kAllWavesXF = 5  // as kAllWaves, quantising before the weights are requested (bf16 activations)
+    kAllWavesXF = 5  // as kAllWaves, quantising before the weights are requested
 };
 
 template <int AM, int NB, int TOK, bool INT_OUT, int FORM, int SG>
@@ -1188,7 +1188,7 @@ void gemv_launch_form(int form, int tok, dim3 grid, dim3 block, size_t lds, hipS
         if (form == kQuantWaves) {
             gemv_launch_tok<AM, NB, false, kQuantWaves, 128>(tok, grid, block, lds, st, a);
         } else if (form == kAllWavesXF) {
-            if constexpr (AM == 0) gemv_launch_tok<AM, NB, false, kAllWavesXF, 128>(tok, grid, block, lds, st, a);
+            gemv_launch_tok<AM, NB, false, kAllWavesXF, 128>(tok, grid, block, lds, st, a);
         } else {
             gemv_launch_tok<AM, NB, false, kAllWaves, 128>(tok, grid, block, lds, st, a);
         }
@@ -1264,12 +1264,12 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
             lds = (size_t)nw * 4 * kWave * sizeof(int);
         }
     }
-    // Fused all-waves form, bf16 activations: quantise before requesting the weights
-    // (kAllWavesXF) when the grid has more 16-row workgroups than CUs and all of them are
-    // resident at once (measured over
-    // 2560..20480 rows x K 2560..4096: 0.1-0.55 us faster there; with at most one workgroup
-    // per CU, or more waves than fit, the serial start costs 0.2-0.45 us instead).
-    if (AM == 0 && form == kAllWaves) {
+    // Fused all-waves form: quantise before requesting the weights (kAllWavesXF) when the
+    // grid has more 16-row workgroups than CUs and all of them are resident at once
+    // (measured with bf16 activations over 2560..20480 rows x K 2560..4096: 0.1-0.55 us
+    // faster there; with at most one workgroup per CU, or more waves than fit, the serial
+    // start costs 0.2-0.45 us instead).
+    if (form == kAllWaves) {
         int dev = 0, ncu = 0, thr = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&

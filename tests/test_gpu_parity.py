@@ -188,7 +188,9 @@ def test_zero_weights_and_zero_tokens(gpu):
 # ------------------------------------------------------------------ fused quantise-and-multiply
 @pytest.mark.parametrize("mode", ["bf16", "f32", "fold", "relu2_glu"])
 @pytest.mark.parametrize("M,N,K", [(1, 48, 384), (2, 272, 2688), (3, 80, 640), (5, 160, 6912), (8, 2064, 2560),
-                                   (16, 32, 128), (1, 64, 12288)])
+                                   (16, 32, 128), (1, 64, 12288),
+                                   # more 16-row workgroups than CUs: the quantise-first form
+                                   (1, 4112, 384), (2, 6912, 2560)])
 def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
     c = wl.small_case(M * 5 + N + K, M, N, K, xkind="t3")
     p, st = pack_dev(c.T, c.S)
@@ -222,7 +224,7 @@ def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
     assert_f32_close(yh, oracle_ref(c.T, c.S, qo, so), f"gemv_act {mode} {M}x{N}x{K}")
 
 
-# With more 16-row workgroups than CUs (all resident), bf16 activations take the form that
+# With more 16-row workgroups than CUs (all resident), the fused step takes the form that
 # quantises before requesting the weights; same arithmetic, so bit-identical to the unfused path.
 @pytest.mark.parametrize("M,N,K", [(1, 4112, 384), (2, 6912, 2560), (1, 13824, 2560), (4, 9216, 1280)])
 def test_gemv_act_quantise_first_form_bitexact(gpu, M, N, K):
