@@ -1207,19 +1207,47 @@ constexpr size_t kMaxLds = 65536;
 #ifndef BITNET_GEMV_MAX_WAVES
 #define BITNET_GEMV_MAX_WAVES 12
 #endif
+// The current device's CU count and the waves it holds at once (CUs x threads
+// per CU / 64); zeros if unknown (then no occupancy-based choice is made).
+struct DeviceSlots {
+    int64_t cus = 0, waves = 0;
+};
+DeviceSlots device_slots() {
+    DeviceSlots d;
+    int dev = 0, ncu = 0, thr = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&thr, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess) {
+        d.cus = ncu;
+        d.waves = (int64_t)ncu * (thr / kWave);
+    }
+    return d;
+}
+
 // Split-K geometry of the decode product: about 4 blocks per wave, at most 12
 // compute waves per workgroup (room for up to 4 quant waves in the fused
-// form), no idle wave.  Every form uses the same geometry and the same
-// summation order, so their fp32 results are bit-identical.
+// form), no idle wave.  If the N/16 workgroups would then not all be resident
+// (slots = the device's wave slots), each wave takes more blocks, up to 8, until
+// they are: 20480x3200 runs 5 waves of 5 blocks instead of 7 waves of 4 (product
+// 6.17 -> 5.70 us, fused step 7.61 -> 6.75 us, 8 tokens 8.58 -> 7.82 us), while
+// grids that fit keep the wider split (fewer, longer waves are slower there).
+// Every form uses the same geometry and the same summation order, so their fp32
+// results are bit-identical.
 constexpr int kMaxSplitWaves = BITNET_GEMV_MAX_WAVES;
 constexpr int kBlocksPerWave = BITNET_GEMV_BLOCKS_PER_WAVE;
-void gemv_split(int K, int *nw_out, int *per_out) {
+void gemv_split(int K, int N, int64_t slots, int *nw_out, int *per_out) {
     const int nblk = K / (int)kBlockK;
     int nw = (nblk + kBlocksPerWave - 1) / kBlocksPerWave;
     if (nw > kMaxSplitWaves) nw = kMaxSplitWaves;
     if (nw < 1) nw = 1;
-    const int per = (nblk + nw - 1) / nw;
-    *nw_out = (nblk + per - 1) / per;
+    int per = (nblk + nw - 1) / nw;
+    nw = (nblk + per - 1) / per;
+    const int64_t wgs = N / kTileN;
+    while (slots > 0 && per < 8 && per < nblk && wgs * nw > slots) {
+        ++per;
+        nw = (nblk + per - 1) / per;
+    }
+    *nw_out = nw;
     *per_out = per;
 }
 
@@ -1228,9 +1256,9 @@ size_t gemv_fused_lds(int M, int K, int nw) { return gemv_fused_region(M, K, nw)
 // Form of the fused quantise-and-multiply launch for activation mode xm (0 bf16,
 // 1 fp32, 2 and 3 two-half fp32): every compute wave quantises its own slice when the
 // tokens' raw chunks fit in registers, else four extra quant waves do it.
-int gemv_fused_form(int xm, int M, int K) {
+int gemv_fused_form(int xm, int M, int K, int N, int64_t slots) {
     int nw, per;
-    gemv_split(K, &nw, &per);
+    gemv_split(K, N, slots, &nw, &per);
     const int tok = M == 1 ? 1 : M == 2 ? 2 : 4;
     return (M <= 4 && allwaves_fits(xm, tok, per < 8 ? per : 8)) ? kAllWaves : kQuantWaves;
 }
@@ -1239,15 +1267,16 @@ int gemv_fused_form(int xm, int M, int K) {
 // form was asked for and does not fit.
 template <int AM, bool INT_OUT, int SG = 128>
 bool gemv_launch(GemvArgs a, hipStream_t st) {
+    const DeviceSlots dev = device_slots();
     int nw, per;
-    gemv_split(a.K, &nw, &per);
+    gemv_split(a.K, a.N, dev.waves, &nw, &per);
     a.per = per;
     a.nwc = nw;
     int form;
     size_t lds;
     if (AM >= 0) {
         if (per > 8) return false;
-        form = gemv_fused_form(AM, a.M, a.K);
+        form = gemv_fused_form(AM, a.M, a.K, a.N, dev.waves);
         a.qw = form == kQuantWaves ? 4 : 0;
         lds = gemv_fused_lds(a.M, a.K, nw);
         if (lds > kMaxLds) return false;
@@ -1269,14 +1298,9 @@ bool gemv_launch(GemvArgs a, hipStream_t st) {
     // (measured with bf16 activations over 2560..20480 rows x K 2560..4096: 0.1-0.55 us
     // faster there; with at most one workgroup per CU, or more waves than fit, the serial
     // start costs 0.2-0.45 us instead).
-    if (form == kAllWaves) {
-        int dev = 0, ncu = 0, thr = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipDeviceGetAttribute(&thr, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess) {
-            const int64_t wgs = a.N / kTileN, waves = wgs * (nw + a.qw);
-            if (wgs > ncu && waves <= (int64_t)ncu * (thr / kWave)) form = kAllWavesXF;
-        }
+    if (form == kAllWaves && dev.cus > 0) {
+        const int64_t wgs = a.N / kTileN, waves = wgs * (nw + a.qw);
+        if (wgs > dev.cus && waves <= dev.waves) form = kAllWavesXF;
     }
     const int nb = per < 8 ? per : 8;
     const int tok = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
@@ -1448,7 +1472,7 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     int nw, per;
-    gemv_split(K, &nw, &per);
+    gemv_split(K, N, device_slots().waves, &nw, &per);
     if (per > 8 || gemv_fused_lds(M, K, nw) > kMaxLds) return BITNET_ERR_UNSUPPORTED_SHAPE;
     GemvArgs a{packed, scales, x, nullptr, y, nullptr, q_out, s_a_out, M, N, K, 0, 0, 0};
     bool ok;
@@ -1538,6 +1562,7 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
 
     const void *in = x;
     int in_dt = xdt;
+    const int64_t slots = device_slots().waves;
     for (int i = 0; i < n; ++i) {
         const bitnet_chain_layer_t &L = layers[i];
         float *out = (i == n - 1) ? y : act[i & 1];
@@ -1545,11 +1570,11 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
                        : L.fold_input == BITNET_JUNCTION_RELU2_GLU ? BITNET_DT_F32_RELU2_GLU
                                                                    : in_dt;
         int nw, per;
-        gemv_split(L.K, &nw, &per);
+        gemv_split(L.K, L.N, slots, &nw, &per);
         // one launch when the cheap fused form applies, else quantise + multiply
         // (the fused form re-quantises in every workgroup: worth it for one or two tokens)
         const bool fused = M <= 2 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
-                           gemv_fused_form(dt, M, L.K) == kAllWaves;
+                           gemv_fused_form(dt, M, L.K, L.N, slots) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
             bool ok;

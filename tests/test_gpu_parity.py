@@ -226,7 +226,9 @@ def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
 
 # With more 16-row workgroups than CUs (all resident), the fused step takes the form that
 # quantises before requesting the weights; same arithmetic, so bit-identical to the unfused path.
-@pytest.mark.parametrize("M,N,K", [(1, 4112, 384), (2, 6912, 2560), (1, 13824, 2560), (4, 9216, 1280)])
+# 20480x3200 takes 5 waves of 5 blocks (the split that keeps all 1280 workgroups resident).
+@pytest.mark.parametrize("M,N,K", [(1, 4112, 384), (2, 6912, 2560), (1, 13824, 2560), (4, 9216, 1280),
+                                   (1, 20480, 3200), (2, 20480, 3200)])
 def test_gemv_act_quantise_first_form_bitexact(gpu, M, N, K):
     assert N // 16 > torch.cuda.get_device_properties(0).multi_processor_count
     c = wl.small_case(M * 7 + N + K, M, N, K, xkind="t3")
