@@ -13,7 +13,8 @@ The roofline object prices the product kernel against 8 TB/s using its
 algorithmic bytes (packed weights + fp32 block scales + int8 activations +
 fp32 outputs) over its own duration, measured with HIP events around graph
 replays on the launch stream; beside it, "attainable_read" is what one bare
-pass of 16-byte loads over the same number of bytes achieves on this GPU.
+pass of 16-byte loads over the same number of bytes achieves on this GPU, and
+"stream_ceiling_1GiB" what the same read sustains over 1 GiB.
 Per-shape results for every decode shape, the prefill product, the format
 variants, the medium batches and the decode stack are reported under "shapes".
 
@@ -40,9 +41,9 @@ ROTATE_BYTES = 2 * LLC_BYTES
 # what the counter reads for a 64 MiB device copy (FETCH_SIZE x 1.999,
 # WRITE_SIZE x 1.000).  Valid only for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha1": "98a1a28352c4ef7a031a6cd43bb5a6d5950f74ad",
-    "bytes_per_launch": 10076428,
-    "fetch_kib": 4895.2, "write_kib": 54.0, "fetch_scale": 1.999, "write_scale": 1.000,
+    "kernel_source_sha1": "d6474f1ff96593a4c657c1cf81513c9b2e62fcf1",
+    "bytes_per_launch": 10076192,
+    "fetch_kib": 4895.1, "write_kib": 54.0, "fetch_scale": 1.999, "write_scale": 1.000,
 }
 
 
@@ -213,6 +214,20 @@ def attainable_read(torch, bn, nbytes, reps=10):
     return {"what": "one pass of 16-byte loads, one per thread, over the same number of bytes, each wave storing "
                     "one word (bitnet_probe_stream_read mode 0); no_output: the same read storing nothing (mode 1)",
             "bytes": n, "us": us, "GBps": n / us / 1e3, "no_output_us": us_noout, "no_output_GBps": n / us_noout / 1e3}
+
+
+def stream_ceiling(torch, bn, reps=5):
+    """Graph-timed one-pass read of 1 GiB (bitnet_probe_stream_read, two buffers
+    alternating, each four times the last-level cache): the streaming-read rate
+    this GPU sustains when launch and ramp costs are amortised."""
+    n = 1 << 30
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sink = torch.empty((bn.lib().bitnet_probe_stream_read_sink_len(n),), dtype=torch.int32, device="cuda")
+    us = graph_us_per_launch(torch, lambda i: bn.bitnet_probe_stream_read(bufs[i % 2], sink, 0), 2, reps)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"what": "one-pass read of 1 GiB, 16-byte loads (bitnet_probe_stream_read mode 0)",
+            "bytes": n, "us": us, "GBps": n / us / 1e3}
 
 
 def prefill_shape(torch, bn, wl, reps=10):
@@ -442,6 +457,8 @@ def main():
     achieved = ab / gemv_us / 1e3
     attain = attainable_read(torch, bn, ab, reps)
     attain["product_frac_of_attainable"] = achieved / attain["GBps"]
+    ceiling = stream_ceiling(torch, bn)
+    ceiling["product_frac_of_ceiling"] = achieved / ceiling["GBps"]
     result = {
         "metric": "W2A8 GEMV packed-weight GB/s, 13824x2560 batch 1 (quantise + product per step)",
         "value": pbytes / (ms_per_step * 1e-3) / 1e9,
@@ -468,12 +485,14 @@ def main():
             "traffic": measured_traffic(), "alg_bytes_per_launch": ab, "kernel_us": gemv_us,
             "packed_GBps_kernel": pbytes / gemv_us / 1e3,
             "attainable_read": attain,
+            "stream_ceiling_1GiB": ceiling,
         },
     }
     log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
         f"gemv {gemv_us:.2f} us, quant {quant_us:.2f} us, two-launch step {step2_us:.2f} us, "
         f"eager step {eager_us:.2f} us; a bare read of the same {attain['bytes']} B takes {attain['us']:.2f} us "
-        f"({attain['GBps']:.0f} GB/s)")
+        f"({attain['GBps']:.0f} GB/s); "
+        f"a 1 GiB read streams at {ceiling['GBps']:.0f} GB/s")
     del d
     torch.cuda.empty_cache()
 

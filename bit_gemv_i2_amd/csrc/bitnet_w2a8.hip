@@ -1226,16 +1226,27 @@ DeviceSlots device_slots() {
 
 // Split-K geometry of the decode product: about 4 blocks per wave, at most 12
 // compute waves per workgroup (room for up to 4 quant waves in the fused
-// form), no idle wave.  If the N/16 workgroups would then not all be resident
-// (slots = the device's wave slots), each wave takes more blocks, up to 8, until
-// they are: 20480x3200 runs 5 waves of 5 blocks instead of 7 waves of 4 (product
-// 6.17 -> 5.70 us, fused step 7.61 -> 6.75 us, 8 tokens 8.58 -> 7.82 us), while
-// grids that fit keep the wider split (fewer, longer waves are slower there).
+// form), no idle wave.  Two occupancy rules refine it (dev = the device's CU
+// count and wave slots; zeros skip them):
+// - at most one workgroup per CU and at least 8 blocks: a CU's four SIMDs
+//   take waves w, w+4, w+8 in turn, so the workgroup lasts as long as its
+//   busiest SIMD, ceil(nw/4) * per blocks; the split minimising that is taken
+//   (ties keep the base split, else take the fewest waves).  Measured (product
+//   / fused step, us): 2560x2560 5x4 -> 4x5 3.12/3.51 -> 2.96/3.34, 8 tokens
+//   3.74 -> 3.41; 2560x3200 7x4 -> 4x7 3.27/3.76 -> 3.07/3.59; 2560x6912
+//   11x5 -> 8x7 3.76/4.92 -> 3.69/4.40; 4096x2560 3.26/3.62 -> 3.07/3.40;
+//   2560x1280 3x4 -> 4x3 fused 2.94 -> 2.86.  Below 8 blocks fixed per-wave
+//   costs dominate (2560x384 as 3 waves of 1 block: fused 2.50 -> 2.59);
+// - more workgroups than the device holds at once: each wave takes more
+//   blocks, up to 8, until all are resident: 20480x3200 runs 5 waves of 5
+//   blocks instead of 7 waves of 4 (product 6.17 -> 5.70 us, fused step 7.61
+//   -> 6.75 us, 8 tokens 8.58 -> 7.82 us).
+// Fused support does not change (per stays <= 8 where the base split has it).
 // Every form uses the same geometry and the same summation order, so their fp32
 // results are bit-identical.
 constexpr int kMaxSplitWaves = BITNET_GEMV_MAX_WAVES;
 constexpr int kBlocksPerWave = BITNET_GEMV_BLOCKS_PER_WAVE;
-void gemv_split(int K, int N, int64_t slots, int *nw_out, int *per_out) {
+void gemv_split(int K, int N, const DeviceSlots &dev, int *nw_out, int *per_out) {
     const int nblk = K / (int)kBlockK;
     int nw = (nblk + kBlocksPerWave - 1) / kBlocksPerWave;
     if (nw > kMaxSplitWaves) nw = kMaxSplitWaves;
@@ -1243,7 +1254,20 @@ void gemv_split(int K, int N, int64_t slots, int *nw_out, int *per_out) {
     int per = (nblk + nw - 1) / nw;
     nw = (nblk + per - 1) / per;
     const int64_t wgs = N / kTileN;
-    while (slots > 0 && per < 8 && per < nblk && wgs * nw > slots) {
+    if (dev.cus > 0 && wgs <= dev.cus && nblk >= 8 && per <= 8) {
+        int best = ((nw + 3) / 4) * per;
+        for (int p = nblk < 8 ? nblk : 8; p >= 1; --p) {  // ties: the base split, else fewer waves
+            const int w = (nblk + p - 1) / p;
+            if (w > kMaxSplitWaves) continue;
+            const int cost = ((w + 3) / 4) * p;
+            if (cost < best) {
+                best = cost;
+                per = p;
+                nw = w;
+            }
+        }
+    }
+    while (dev.waves > 0 && per < 8 && per < nblk && wgs * nw > dev.waves) {
         ++per;
         nw = (nblk + per - 1) / per;
     }
@@ -1256,9 +1280,9 @@ size_t gemv_fused_lds(int M, int K, int nw) { return gemv_fused_region(M, K, nw)
 // Form of the fused quantise-and-multiply launch for activation mode xm (0 bf16,
 // 1 fp32, 2 and 3 two-half fp32): every compute wave quantises its own slice when the
 // tokens' raw chunks fit in registers, else four extra quant waves do it.
-int gemv_fused_form(int xm, int M, int K, int N, int64_t slots) {
+int gemv_fused_form(int xm, int M, int K, int N, const DeviceSlots &dev) {
     int nw, per;
-    gemv_split(K, N, slots, &nw, &per);
+    gemv_split(K, N, dev, &nw, &per);
     const int tok = M == 1 ? 1 : M == 2 ? 2 : 4;
     return (M <= 4 && allwaves_fits(xm, tok, per < 8 ? per : 8)) ? kAllWaves : kQuantWaves;
 }
@@ -1269,14 +1293,14 @@ template <int AM, bool INT_OUT, int SG = 128>
 bool gemv_launch(GemvArgs a, hipStream_t st) {
     const DeviceSlots dev = device_slots();
     int nw, per;
-    gemv_split(a.K, a.N, dev.waves, &nw, &per);
+    gemv_split(a.K, a.N, dev, &nw, &per);
     a.per = per;
     a.nwc = nw;
     int form;
     size_t lds;
     if (AM >= 0) {
         if (per > 8) return false;
-        form = gemv_fused_form(AM, a.M, a.K, a.N, dev.waves);
+        form = gemv_fused_form(AM, a.M, a.K, a.N, dev);
         a.qw = form == kQuantWaves ? 4 : 0;
         lds = gemv_fused_lds(a.M, a.K, nw);
         if (lds > kMaxLds) return false;
@@ -1472,7 +1496,7 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     int nw, per;
-    gemv_split(K, N, device_slots().waves, &nw, &per);
+    gemv_split(K, N, device_slots(), &nw, &per);
     if (per > 8 || gemv_fused_lds(M, K, nw) > kMaxLds) return BITNET_ERR_UNSUPPORTED_SHAPE;
     GemvArgs a{packed, scales, x, nullptr, y, nullptr, q_out, s_a_out, M, N, K, 0, 0, 0};
     bool ok;
@@ -1562,7 +1586,7 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
 
     const void *in = x;
     int in_dt = xdt;
-    const int64_t slots = device_slots().waves;
+    const DeviceSlots dev = device_slots();
     for (int i = 0; i < n; ++i) {
         const bitnet_chain_layer_t &L = layers[i];
         float *out = (i == n - 1) ? y : act[i & 1];
@@ -1570,11 +1594,11 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
                        : L.fold_input == BITNET_JUNCTION_RELU2_GLU ? BITNET_DT_F32_RELU2_GLU
                                                                    : in_dt;
         int nw, per;
-        gemv_split(L.K, L.N, slots, &nw, &per);
+        gemv_split(L.K, L.N, dev, &nw, &per);
         // one launch when the cheap fused form applies, else quantise + multiply
         // (the fused form re-quantises in every workgroup: worth it for one or two tokens)
         const bool fused = M <= 2 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
-                           gemv_fused_form(dt, M, L.K, L.N, slots) == kAllWaves;
+                           gemv_fused_form(dt, M, L.K, L.N, dev) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};
             bool ok;

@@ -190,7 +190,10 @@ def test_zero_weights_and_zero_tokens(gpu):
 @pytest.mark.parametrize("M,N,K", [(1, 48, 384), (2, 272, 2688), (3, 80, 640), (5, 160, 6912), (8, 2064, 2560),
                                    (16, 32, 128), (1, 64, 12288),
                                    # more 16-row workgroups than CUs: the quantise-first form
-                                   (1, 4112, 384), (2, 6912, 2560)])
+                                   (1, 4112, 384), (2, 6912, 2560),
+                                   # at most one workgroup per CU: busiest-SIMD splits
+                                   # (waves x blocks 4x7, 4x3, 4x5)
+                                   (1, 2560, 3200), (1, 2560, 1280), (8, 2560, 2560)])
 def test_gemv_act_matches_oracle_and_unfused(gpu, mode, M, N, K):
     c = wl.small_case(M * 5 + N + K, M, N, K, xkind="t3")
     p, st = pack_dev(c.T, c.S)
