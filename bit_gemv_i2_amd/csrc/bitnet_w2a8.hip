@@ -20,6 +20,7 @@
 // the int32 tile is drained into fp32 with the block scale.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "bitnet_w2a8.h"
@@ -1207,19 +1208,37 @@ constexpr size_t kMaxLds = 65536;
 #ifndef BITNET_GEMV_MAX_WAVES
 #define BITNET_GEMV_MAX_WAVES 12
 #endif
-// The current device's CU count and the waves it holds at once (CUs x threads
-// per CU / 64); zeros if unknown (then no occupancy-based choice is made).
+// CU count and the waves held at once (CUs x threads per CU / 64) of the
+// device that `st` belongs to; zeros if unknown (then no occupancy-based choice
+// is made).  Read once per device and cached (the values never change while the
+// process runs), so a launch costs no attribute queries.
 struct DeviceSlots {
     int64_t cus = 0, waves = 0;
 };
-DeviceSlots device_slots() {
+constexpr int kSlotCacheDevices = 64;
+std::atomic<int64_t> g_slot_cus[kSlotCacheDevices], g_slot_waves[kSlotCacheDevices];
+DeviceSlots device_slots(hipStream_t st) {
     DeviceSlots d;
-    int dev = 0, ncu = 0, thr = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipDeviceGetAttribute(&thr, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess) {
+    int dev = 0;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) return d;
+    const bool cached = dev >= 0 && dev < kSlotCacheDevices;
+    if (cached) {
+        d.waves = g_slot_waves[dev].load(std::memory_order_acquire);
+        if (d.waves > 0) {
+            d.cus = g_slot_cus[dev].load(std::memory_order_relaxed);
+            return d;
+        }
+    }
+    int ncu = 0, thr = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&thr, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess &&
+        ncu > 0 && thr >= kWave) {
         d.cus = ncu;
         d.waves = (int64_t)ncu * (thr / kWave);
+        if (cached) {
+            g_slot_cus[dev].store(d.cus, std::memory_order_relaxed);
+            g_slot_waves[dev].store(d.waves, std::memory_order_release);
+        }
     }
     return d;
 }
@@ -1291,7 +1310,7 @@ int gemv_fused_form(int xm, int M, int K, int N, const DeviceSlots &dev) {
 // form was asked for and does not fit.
 template <int AM, bool INT_OUT, int SG = 128>
 bool gemv_launch(GemvArgs a, hipStream_t st) {
-    const DeviceSlots dev = device_slots();
+    const DeviceSlots dev = device_slots(st);
     int nw, per;
     gemv_split(a.K, a.N, dev, &nw, &per);
     a.per = per;
@@ -1496,7 +1515,7 @@ bitnet_status_t bitnet_w2a8_gemv_act(const uint8_t *packed, const float *scales,
         return BITNET_ERR_INVALID_ARG;
     if (!shape_ok(N, K) || M < 1 || M > kGemvMaxM) return BITNET_ERR_UNSUPPORTED_SHAPE;
     int nw, per;
-    gemv_split(K, N, device_slots(), &nw, &per);
+    gemv_split(K, N, device_slots(stream), &nw, &per);
     if (per > 8 || gemv_fused_lds(M, K, nw) > kMaxLds) return BITNET_ERR_UNSUPPORTED_SHAPE;
     GemvArgs a{packed, scales, x, nullptr, y, nullptr, q_out, s_a_out, M, N, K, 0, 0, 0};
     bool ok;
@@ -1586,7 +1605,7 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
 
     const void *in = x;
     int in_dt = xdt;
-    const DeviceSlots dev = device_slots();
+    const DeviceSlots dev = device_slots(stream);
     for (int i = 0; i < n; ++i) {
         const bitnet_chain_layer_t &L = layers[i];
         float *out = (i == n - 1) ? y : act[i & 1];

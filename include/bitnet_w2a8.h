@@ -28,7 +28,8 @@
  *     without synchronising; a launch failure is reported as BITNET_ERR_HIP.
  *     No C++ exception crosses this interface.
  *   - Ownership: the caller owns every buffer.  The library allocates no
- *     memory, keeps no state between calls and is re-entrant.
+ *     memory and is re-entrant; the only state it keeps between calls is a
+ *     cache of each device's CU count and wave slots, read on first use.
  *   - "device" pointers are HIP device memory, 16-byte aligned; "host"
  *     pointers are ordinary host memory.  Non-finite inputs are outside the
  *     contract.
@@ -213,7 +214,9 @@ bitnet_status_t bitnet_quant_act_relu2_glu(const float *y, int M, int H, int8_t 
  *   y       device, fp32 [M][N] (out)
  * Rules: 1 <= M <= 16 and the shape rules.  The fp32 epilogue's summation order
  * is unspecified: y agrees with the exact value within 1e-5 of
- * max(|y|, s_a * sum_b |S*A|). */
+ * max(|y|, s_a * sum_b |S*A|).  The split of K over waves, and with it the
+ * order, depends on the shape and on the device's CU count and wave slots, so
+ * on one device the result of a shape is always the same. */
 bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q,
                                  const float *s_a, float *y, int M, int N, int K, hipStream_t stream);
 
