@@ -47,6 +47,8 @@ _lib = None
 _SIGS = {
     "bitnet_status_str": ([ctypes.c_int], ctypes.c_char_p),
     "bitnet_check_shape": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
+    "bitnet_gemv_split": ([ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "bitnet_packed_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
     "bitnet_scale_count": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
     "bitnet_ternarize_absmean": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -140,6 +142,15 @@ def bitnet_status_str(status: int) -> str:
 
 def bitnet_check_shape(N: int, K: int) -> int:
     return lib().bitnet_check_shape(N, K)
+
+
+def bitnet_gemv_split(N: int, K: int, cus: int = 0, wave_slots: int = 0):
+    """(waves per 16-row workgroup, 128-weight blocks per wave) of the decode products for an
+    N x K matrix on a device with `cus` CUs holding `wave_slots` waves (0, 0: the base split)."""
+    w, p = ctypes.c_int(0), ctypes.c_int(0)
+    _ok(lib().bitnet_gemv_split(int(N), int(K), int(cus), int(wave_slots), ctypes.byref(w), ctypes.byref(p)),
+        "bitnet_gemv_split")
+    return w.value, p.value
 
 
 def bitnet_packed_bytes(N: int, K: int) -> int:

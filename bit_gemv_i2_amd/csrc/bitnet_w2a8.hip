@@ -1420,6 +1420,17 @@ const char *bitnet_status_str(int status) {
     }
 }
 
+bitnet_status_t bitnet_gemv_split(int N, int K, int64_t cus, int64_t wave_slots, int *waves,
+                                  int *blocks_per_wave) {
+    if (!waves || !blocks_per_wave || cus < 0 || wave_slots < 0) return BITNET_ERR_INVALID_ARG;
+    if (!shape_ok(N, K)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    DeviceSlots dev;
+    dev.cus = cus;
+    dev.waves = wave_slots;
+    gemv_split(K, N, dev, waves, blocks_per_wave);
+    return BITNET_OK;
+}
+
 bitnet_status_t bitnet_quant_act(const void *x, int xdt, int M, int K, int8_t *q, float *s_a,
                                  hipStream_t stream) {
     if (!x || !q || !s_a || !aligned(x, 16) || !aligned(q, 16) || !aligned(s_a, 4)) return BITNET_ERR_INVALID_ARG;

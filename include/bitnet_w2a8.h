@@ -220,6 +220,17 @@ bitnet_status_t bitnet_quant_act_relu2_glu(const float *y, int M, int H, int8_t 
 bitnet_status_t bitnet_w2a8_gemv(const uint8_t *packed, const float *scales, const int8_t *q,
                                  const float *s_a, float *y, int M, int N, int K, hipStream_t stream);
 
+/* Split-K geometry of the decode products (bitnet_w2a8_gemv[_g], bitnet_w2a8_gemv_act and
+ * the chain) for an N x K weight matrix on a device with `cus` compute units that hold
+ * `wave_slots` waves at once (0 and 0: unknown, the base split): the waves per 16-row
+ * workgroup and the 128-weight blocks each wave sums.  The geometry fixes the fp32
+ * summation order of y.  Host only, makes no HIP call.
+ *   waves, blocks_per_wave  host, one int each (out)
+ * Rules: the shape rules (else UNSUPPORTED_SHAPE); non-null outputs and cus,
+ * wave_slots >= 0 (else INVALID_ARG). */
+bitnet_status_t bitnet_gemv_split(int N, int K, int64_t cus, int64_t wave_slots, int *waves,
+                                  int *blocks_per_wave);
+
 /* Decode step in one launch: quantise the activations exactly as
  * bitnet_quant_act does (per-token absmax, fp32, half to even) and multiply, as
  * bitnet_w2a8_gemv does.  Each workgroup derives the same int8 values and

@@ -52,6 +52,67 @@ def test_shape_rules_and_sizes(N, K, ok):
     assert bn.bitnet_scale_count(N, K) == (N * K // 128 if ok else 0)
 
 
+# ------------------------------------------------------------------ decode split-K geometry (host logic)
+MI355X_CUS, MI355X_SLOTS = 256, 256 * 32  # 256 CUs x 2048 threads / 64
+
+
+# waves x blocks per wave on a 256-CU device, as measured best (at most one 16-row workgroup
+# per CU: busiest SIMD ceil(waves/4) x blocks; more workgroups than fit: blocks grow until
+# every workgroup is resident; otherwise about 4 blocks per wave)
+@pytest.mark.parametrize("N,K,want", [(2560, 2560, (4, 5)), (2560, 3200, (4, 7)), (2560, 6912, (8, 7)),
+                                      (2560, 1280, (4, 3)), (4096, 2560, (4, 5)), (2560, 4096, (8, 4)),
+                                      (4096, 1664, (4, 4)), (2560, 384, (1, 3)), (13824, 2560, (5, 4)),
+                                      (20480, 3200, (5, 5)), (6912, 2560, (5, 4)), (2560, 12416, (11, 9))])
+def test_gemv_split_on_a_256_cu_device(N, K, want):
+    assert bn.bitnet_gemv_split(N, K, MI355X_CUS, MI355X_SLOTS) == want
+
+
+@pytest.mark.parametrize("N,K,want", [(2560, 2560, (5, 4)), (20480, 3200, (7, 4)), (2560, 6912, (11, 5)),
+                                      (16, 128, (1, 1)), (16, 12288, (12, 8))])
+def test_gemv_split_without_device_information_is_the_base_split(N, K, want):
+    assert bn.bitnet_gemv_split(N, K) == want
+
+
+def _busiest_simd(w, p):
+    return -(-w // 4) * p
+
+
+@pytest.mark.parametrize("cus", [0, 32, 80, 256, 304])
+def test_gemv_split_invariants(cus):
+    slots = cus * 32
+    for K in range(128, 12416 + 1, 128 * 3):
+        nblk = K // 128
+        base_w, base_p = bn.bitnet_gemv_split(16, K)
+        for N in (16, 1024, 2560, 4096, 8192, 13824, 20480, 40960):
+            w, p = bn.bitnet_gemv_split(N, K, cus, slots)
+            assert 1 <= w <= 12 and p >= 1
+            assert (w - 1) * p < nblk <= w * p, (N, K, w, p)  # every block covered, no idle wave
+            if base_p <= 8:
+                assert p <= 8, (N, K, w, p)  # fused forms stay available
+            wgs = N // 16
+            if cus and wgs <= cus and nblk >= 8 and base_p <= 8:
+                # no split within the limits has a less loaded SIMD
+                best = min(_busiest_simd(-(-nblk // q), q) for q in range(1, min(8, nblk) + 1)
+                           if -(-nblk // q) <= 12)
+                assert _busiest_simd(w, p) == best, (N, K, w, p, best)
+            if cus and wgs > cus and p < min(8, nblk):
+                assert wgs * w <= slots, (N, K, w, p)  # the whole grid is resident
+            if not cus:
+                assert (w, p) == (base_w, base_p)
+
+
+def test_gemv_split_rejects_bad_arguments():
+    for N, K in [(8, 128), (2560, 2500)]:
+        with pytest.raises(bn.BitnetError) as ei:
+            bn.bitnet_gemv_split(N, K, MI355X_CUS, MI355X_SLOTS)
+        assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(bn.BitnetError) as ei:
+        bn.bitnet_gemv_split(2560, 2560, -1, MI355X_SLOTS)
+    assert ei.value.status == bn.BITNET_ERR_INVALID_ARG
+    w = ctypes.c_int(0)
+    assert bn.lib().bitnet_gemv_split(2560, 2560, 0, 0, None, ctypes.byref(w)) == bn.BITNET_ERR_INVALID_ARG
+
+
 # ------------------------------------------------------------------ host offline code vs oracle
 @pytest.mark.parametrize("seed,N,K", [(0, 16, 128), (1, 48, 384), (2, 2560, 2560), (3, 13824, 2560)])
 def test_ternarize_matches_oracle(seed, N, K):
