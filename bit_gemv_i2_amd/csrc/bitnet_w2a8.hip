@@ -320,7 +320,7 @@ __device__ void quant_wave(const GemvArgs &args, int8_t *qs, float *sa_lds, int 
 enum GemvForm {
     kDirect = 0,    // int8 q from global memory, one chunk of blocks per wave
     kMulti = 1,     // as kDirect with a loop over chunks (K beyond 12 x 8 blocks)
-    kStaged = 2,    // int8 q slice fetched with a few coalesced loads into LDS (M <= 4)
+    kStaged = 2,    // int8 q slice fetched with a few coalesced loads into LDS (when it fits)
     kAllWaves = 3,  // fused quantisation, every compute wave quantises its own K-slice (M <= 4)
     kQuantWaves = 4, // fused quantisation by 4 extra quant waves (4 < M <= 16)
     kAllWavesXF = 5  // as kAllWaves, quantising before the weights are requested
