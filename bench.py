@@ -470,7 +470,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 x ternary -> int32, fp32 epilogue",
+        "dtype": "int8",
+        "arithmetic": "int8 activations x ternary weights -> int32 per 128-weight block, fp32 epilogue",
         "data": "synthetic (seeded; absmean-ternarised N(0,0.02) weights, N(0,1) bf16 activations)",
         "config": {"workload": "gemv_13824x2560_m1", "M": M, "N": N, "K": K,
                    "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32)},
