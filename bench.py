@@ -17,6 +17,8 @@ pass of 16-byte loads over the same number of bytes achieves on this GPU, and
 "stream_ceiling_1GiB" what the same read sustains over 1 GiB.
 Per-shape results for every decode shape, the prefill product, the format
 variants, the medium batches and the decode stack are reported under "shapes".
+"cpu_baseline" is the CPU oracle, single-threaded, on the headline workload;
+"cpu_baseline_all_cores" the same oracle in one process per host core.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
 """
@@ -344,6 +346,47 @@ def medium_batch_shapes(torch, bn, wl, reps=10):
 
 
 # ----------------------------------------------------------------------------
+def _oracle_passes(args):
+    """One host core: the oracle's quantise + product passes on the headline
+    workload for about `seconds` (runs in a process of its own)."""
+    core, P, S, x_bits, N, K, seconds = args
+    try:
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        pass
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        q, s = oracle.quant_act_bf16(x_bits)
+        oracle.w2a8(P, S, q, s, N, K)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return reps, el
+
+
+def cpu_baseline_all_cores(c, T, S, seconds, cores):
+    """The same oracle on every host core this process may use (at most 16): one
+    process per core, each running independent single-threaded passes; the
+    aggregate rate of all of them."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    import oracle
+    P = oracle.pack_i2s(T)
+    use = list(cores)[:16]
+    # fresh interpreters that never touch the GPU; a worker that fails raises here
+    with ProcessPoolExecutor(max_workers=len(use), mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_passes, [(k, P, S, c.x_bits, c.N, c.K, seconds) for k in use],
+                          timeout=seconds + 120))
+    reps = sum(r for r, _ in res)
+    wall = max(e for _, e in res)
+    return {
+        "value": reps * (c.N * c.K // 4) / wall / 1e9, "unit": "GB/s", "cores": len(use), "kind": "oracle",
+        "sample": f"{reps} full quantise+product passes of the 13824x2560 M=1 workload in {len(use)} "
+                  f"processes, one pinned to each core, {wall:.1f} s",
+    }
+
+
 def cpu_baseline(wl, c, T, S, seconds):
     """The oracle, as it stands, timed single-threaded on this host on the
     headline workload (quantise + product of the whole 13824x2560 matrix)."""
@@ -532,6 +575,8 @@ def main():
         result["shapes"] = shapes
 
     if not args.no_cpu:
+        cores = sorted(os.sched_getaffinity(0))
+        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(c, T, S, min(args.cpu_seconds, 8.0), cores)
         result["cpu_baseline"] = cpu_baseline(wl, c, T, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
