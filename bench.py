@@ -486,6 +486,8 @@ def main():
     g = capture(torch, d.fused, args.steps)
     total_ms = time_graph(torch, g, 1)
     ms_per_step = total_ms / args.steps
+    # spread: ten more timed replays of the same graph (not part of `value`)
+    rep_us = sorted(time_graph(torch, g, 1) * 1e3 / args.steps for _ in range(10))
     del g
     # the product kernel alone (pre-quantised input): one graph over the weight rotation
     reps = max(1, args.steps // d.rot.R)
@@ -519,6 +521,8 @@ def main():
         "config": {"workload": "gemv_13824x2560_m1", "M": M, "N": N, "K": K,
                    "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32)},
         "step_us": ms_per_step * 1e3,
+        "step_us_repeats": {"n": len(rep_us), "median": (rep_us[4] + rep_us[5]) / 2, "min": rep_us[0],
+                            "max": rep_us[-1]},
         "pct_hbm_packed_step": 100.0 * pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "quant_us": quant_us,
         "step_two_launch_us": step2_us,
