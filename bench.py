@@ -2,19 +2,22 @@
 """Benchmark of the W2A8 ternary decode product on one MI355X.
 
 One step = one pass of the decode hot path over one batch: per-token int8
-quantisation of the bf16 activations (bitnet_quant_act) followed by the W2A8
-product (bitnet_w2a8_gemv), for the 13824x2560 fused gate+up shape at batch 1
-(weights from absmean-ternarised N(0, 0.02), activations N(0,1) bf16).  Every
-step reads a different copy of the packed weights, from a rotation larger than
-twice the 256 MB last-level cache, so the weight stream comes from HBM.
+quantisation of the bf16 activations and the W2A8 product, for the 13824x2560
+fused gate+up shape at batch 1 (weights from absmean-ternarised N(0, 0.02),
+activations N(0,1) bf16), as one fused launch (bitnet_w2a8_gemv_act, which
+quantises exactly as bitnet_quant_act and multiplies as bitnet_w2a8_gemv).
+Every step reads a different copy of the packed weights, from a rotation larger
+than twice the 256 MB last-level cache, so the weight stream comes from HBM.
 
 value = packed-weight bytes (N*K/4) per step / step time, in GB/s.
-The roofline object prices the product kernel against 8 TB/s using its
-algorithmic bytes (packed weights + fp32 block scales + int8 activations +
-fp32 outputs) over its own duration, measured with HIP events around graph
-replays on the launch stream; beside it, "attainable_read" is what one bare
-pass of 16-byte loads over the same number of bytes achieves on this GPU, and
-"stream_ceiling_1GiB" what the same read sustains over 1 GiB.
+The roofline object prices the step's kernel against 8 TB/s using its
+algorithmic bytes (packed weights + fp32 block scales + bf16 activations +
+fp32 outputs) over its average duration in the timed region (HIP events on the
+launch stream around the captured steps, one launch each); "product_kernel"
+gives the same for the product alone (int8 q in).  Beside them,
+"attainable_read" is what one bare pass of 16-byte loads over the same number
+of bytes achieves on this GPU, and "stream_ceiling_1GiB" what the same read
+sustains over 1 GiB.
 Per-shape results for every decode shape, the prefill product, the format
 variants, the medium batches and the decode stack are reported under "shapes".
 "cpu_baseline" is the CPU oracle, single-threaded, on the headline workload;
@@ -38,26 +41,29 @@ INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix-core peak, published
 LLC_BYTES = 256 << 20          # Infinity Cache
 ROTATE_BYTES = 2 * LLC_BYTES
 
-# HBM bytes per launch of the headline product kernel, from two rocprofv3 --pmc
-# passes (FETCH_SIZE, WRITE_SIZE) over `bench.py --profile-run`, each scaled by
-# what the counter reads for a 64 MiB device copy (FETCH_SIZE x 1.999,
-# WRITE_SIZE x 1.000).  Valid only for the kernel source it was taken on.
+# HBM bytes per launch of the headline kernels (the fused quantise-and-multiply
+# step and the product alone), from two rocprofv3 --pmc passes (FETCH_SIZE,
+# WRITE_SIZE) over `bench.py --profile-run`, each scaled by what the counter reads
+# for a 64 MiB device copy (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000).  Valid only
+# for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
     "kernel_source_sha1": "031649b2162bb6913f8d5736fa7df7e52da27e73",
-    "bytes_per_launch": 10076945,
-    "fetch_kib": 4895.3, "write_kib": 54.0, "fetch_scale": 1.999, "write_scale": 1.000,
+    "fused": {"bytes_per_launch": 10109087, "fetch_kib": 4911.0, "write_kib": 54.0},
+    "product": {"bytes_per_launch": 10076945, "fetch_kib": 4895.3, "write_kib": 54.0},
+    "fetch_scale": 1.999, "write_scale": 1.000,
 }
 
 
-def measured_traffic():
-    """The counter-measured bytes, or None if the kernel source changed since."""
+def measured_traffic(kernel):
+    """The counter-measured bytes of `kernel` ("fused" or "product"), or None if the
+    kernel source changed since they were taken."""
     import hashlib
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_gemv_i2_amd", "csrc", "bitnet_w2a8.hip")
     try:
         sha = hashlib.sha1(open(path, "rb").read()).hexdigest()
     except OSError:
         return None
-    return MEASURED_TRAFFIC["bytes_per_launch"] if sha == MEASURED_TRAFFIC["kernel_source_sha1"] else None
+    return MEASURED_TRAFFIC[kernel]["bytes_per_launch"] if sha == MEASURED_TRAFFIC["kernel_source_sha1"] else None
 
 
 def log(*a):
@@ -499,11 +505,15 @@ def main():
     N, K, M = c.N, c.K, c.M
     pbytes = N * K // 4
     ab = gemv_bytes(M, N, K)
-    achieved = ab / gemv_us / 1e3
-    attain = attainable_read(torch, bn, ab, reps)
-    attain["product_frac_of_attainable"] = achieved / attain["GBps"]
+    ab_fused = ab + M * K  # bf16 activations (2 bytes a value) instead of int8 q
+    step_us = ms_per_step * 1e3  # one fused launch per step: its average duration over the timed region
+    achieved = ab_fused / step_us / 1e3
+    achieved_product = ab / gemv_us / 1e3
+    attain = attainable_read(torch, bn, ab_fused, reps)
+    attain["fused_frac_of_attainable"] = achieved / attain["GBps"]
+    attain["product_frac_of_attainable"] = achieved_product / attain["GBps"]
     ceiling = stream_ceiling(torch, bn)
-    ceiling["product_frac_of_ceiling"] = achieved / ceiling["GBps"]
+    ceiling["fused_frac_of_ceiling"] = achieved / ceiling["GBps"]
     result = {
         "metric": "W2A8 GEMV packed-weight GB/s, 13824x2560 batch 1 (quantise + product per step)",
         "value": pbytes / (ms_per_step * 1e-3) / 1e9,
@@ -528,12 +538,18 @@ def main():
         "step_two_launch_us": step2_us,
         "eager_step_us": eager_us,
         "roofline": {
-            "bound": "hbm", "kernel": "gemv_kernel (bitnet_w2a8_gemv)",
+            "bound": "hbm",
+            "kernel": "gemv_kernel, fused quantise-and-multiply form (bitnet_w2a8_gemv_act): the step's one launch",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(), "alg_bytes_per_launch": ab, "kernel_us": gemv_us,
-            "packed_GBps_kernel": pbytes / gemv_us / 1e3,
+            "traffic": measured_traffic("fused"), "alg_bytes_per_launch": ab_fused, "kernel_us": step_us,
             "attainable_read": attain,
             "stream_ceiling_1GiB": ceiling,
+            "product_kernel": {
+                "kernel": "gemv_kernel (bitnet_w2a8_gemv, int8 q in), graph-timed over the weight rotation",
+                "achieved": achieved_product, "frac": achieved_product / HBM_PEAK_GBS, "kernel_us": gemv_us,
+                "alg_bytes_per_launch": ab, "traffic": measured_traffic("product"),
+                "packed_GBps_kernel": pbytes / gemv_us / 1e3,
+            },
         },
     }
     log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
