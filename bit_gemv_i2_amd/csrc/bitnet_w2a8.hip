@@ -631,7 +631,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // weights per scale (scales staged per block: [tile][16 rows] or
 // [tile][16 rows][2 halves]) or 0 (one scale: integer sums over all of K,
 // scaled once in the epilogue).
-template <int OUT, int SG, int RT>
+// KS (at most 64 tokens, RT <= 2, SG 128 or 0): the token tile's second half
+// would hold no tokens, so each pipeline stage carries two blocks instead: LDS
+// rows 64..127 of the activation tile, and the brick and scale slots past the
+// first 4*RT tiles, hold the odd block for tokens 0..63.  Waves wm = 0 sum the
+// even blocks, wm = 1 the odd ones; the two partial sums are added once, through
+// LDS, before the epilogue (a fixed order, so results are deterministic).
+template <int OUT, int SG, int RT, bool KS = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                              const float *__restrict__ scales,
                                                              const int8_t *__restrict__ q,
@@ -641,6 +647,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     constexpr int SPT = SG == 64 ? 2 : 1;             // scales per row and 128-block
     constexpr int SST = BLOCKED ? kSStage * SPT : 0;  // staged scale bytes per block
     constexpr int STAGE = kAStage + kBStage + SST;
+    static_assert(!KS || (RT <= 2 && SG != 64), "two-block stages: up to 2 row tiles, one scale per block");
     __shared__ __align__(16) unsigned char lds[2 * STAGE];
     const int G = gridDim.x;
     int t = blockIdx.x;
@@ -652,9 +659,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     const int l = tid & 63, g = l >> 4, j = l & 15;
     const int wm = w >> 2, wn = w & 3;
     const int nblk = K >> 7, ntile_n = N >> 4;
+    const int nst = KS ? (nblk + 1) >> 1 : nblk;  // pipeline stages (KS: two blocks each)
+    constexpr int NSLOT = (KS ? 2 : 1) * 4 * RT;  // brick / scale tile slots per stage
 
-    // staging assignment (global -> registers -> LDS)
-    int arow[2], acol[2];
+    // staging assignment (global -> registers -> LDS); KS: the second half of the
+    // activation rows and of the slots carries the stage's odd block
+    int arow[2], acol[2], ahalf[2];
     const int8_t *aptr[2];
     bool aok[2];
 #pragma unroll
@@ -662,17 +672,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         const int c = tid + kGemmThreads * r;
         arow[r] = c >> 3;
         acol[r] = (c & 7) * 16;
-        const int tok = m0 + arow[r];
+        ahalf[r] = KS ? arow[r] >> 6 : 0;
+        const int tok = m0 + (KS ? arow[r] & 63 : arow[r]);
         aok[r] = tok < M;
         aptr[r] = q + (size_t)(aok[r] ? tok : 0) * K + acol[r];
     }
-    const int bT = T0 + min(tid >> 5, 4 * RT - 1);  // threads past the tile's bricks repeat the last
+    const int bslot = min(tid >> 5, NSLOT - 1);  // threads past the stage's bricks repeat the last
+    const int bhalf = bslot / (4 * RT);
+    const int bT = T0 + bslot % (4 * RT);
     const bool bok = bT < ntile_n;
     const uint8_t *bptr = packed + (size_t)(bok ? bT : 0) * nblk * kBrickBytes + (tid & 31) * 16;
     // scale staging: 64 (SG 128) or 128 (SG 64) threads, one float4 each per block
     constexpr int SCT = 4 * SPT;  // staging threads per tile
     // threads past the 4*RT tiles' scales repeat the last tile's (not stored)
-    const int sT = T0 + min(tid / SCT, 4 * RT - 1);
+    const int sslot = min(tid / SCT, NSLOT - 1);
+    const int shalf = sslot / (4 * RT);
+    const int sT = T0 + sslot % (4 * RT);
     const bool sok = BLOCKED && sT < ntile_n;
     const float *sptr = scales + (size_t)(sok ? sT : 0) * nblk * kTileN * SPT + (tid % SCT) * 4;
 
@@ -689,20 +704,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     // tile 0, whose products land in outputs that are never stored): branch-free
     // issue lets the wait counters track each block's loads exactly, so the
     // store of block b+1 does not wait for the prefetch of block b+2.
-    auto gload = [&](int b, Staged &r) {
-        b = min(b, nblk - 1);
+    auto gload = [&](int b, Staged &r) {  // b: pipeline stage
+        b = min(b, nst - 1);
+        auto blk = [&](int half) { return KS ? min(2 * b + half, nblk - 1) : b; };
 #pragma unroll
-        for (int i = 0; i < 2; ++i) r.a[i] = *reinterpret_cast<const v4i *>(aptr[i] + (size_t)b * kBlockK);
-        r.b = *reinterpret_cast<const v4i *>(bptr + (size_t)b * kBrickBytes);
-        if (BLOCKED) r.s = *reinterpret_cast<const v4f *>(sptr + (size_t)b * kTileN * SPT);
+        for (int i = 0; i < 2; ++i)
+            r.a[i] = *reinterpret_cast<const v4i *>(aptr[i] + (size_t)blk(ahalf[i]) * kBlockK);
+        r.b = *reinterpret_cast<const v4i *>(bptr + (size_t)blk(bhalf) * kBrickBytes);
+        if (BLOCKED) r.s = *reinterpret_cast<const v4f *>(sptr + (size_t)blk(shalf) * kTileN * SPT);
     };
     auto lstore = [&](int st, const Staged &r) {
         unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(base + arow[i] * kAStride + acol[i]) = r.a[i];
-        if (tid < 128 * RT) *reinterpret_cast<v4i *>(base + kAStage + tid * 16) = r.b;
+        if (tid < 32 * NSLOT) *reinterpret_cast<v4i *>(base + kAStage + tid * 16) = r.b;
         // LDS scales: [half][16 tiles][16 rows]; global SG 64 order is [tile][row][half]
-        if (BLOCKED && tid < 4 * RT * SCT) {
+        if (BLOCKED && tid < NSLOT * SCT) {
             float *sb = reinterpret_cast<float *>(base + kAStage + kBStage);
             if constexpr (SG == 128) {
                 *reinterpret_cast<v4f *>(sb + 4 * tid) = r.s;
@@ -737,7 +754,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
                 ao[ti][s] = *reinterpret_cast<const v4i *>(base + (64 * wm + 16 * ti + j) * kAStride + 64 * s + 16 * g);
 #pragma unroll
         for (int tj = 0; tj < RT; ++tj) {
-            const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + (RT * wn + tj) * 512 + l * 8);
+            const int slot = (KS ? 4 * RT * wm : 0) + RT * wn + tj;
+            const uint2 wv = *reinterpret_cast<const uint2 *>(base + kAStage + slot * 512 + l * 8);
             bw[tj][0] = decode16(wv.x);
             bw[tj][1] = decode16(wv.y);
         }
@@ -747,8 +765,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
         const unsigned char *base = lds + st * STAGE;
 #pragma unroll
         for (int tj = 0; tj < RT; ++tj) {
+            const int slot = (KS ? 4 * RT * wm : 0) + RT * wn + tj;
             const float4 s4 = *reinterpret_cast<const float4 *>(base + kAStage + kBStage + h * 1024 +
-                                                                ((RT * wn + tj) * 16 + 4 * g) * 4);
+                                                                (slot * 16 + 4 * g) * 4);
             sc[tj][0] = s4.x;
             sc[tj][1] = s4.y;
             sc[tj][2] = s4.z;
@@ -826,25 +845,51 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     // written out with fixed register sets (no pointer selects between them).
     // Waves whose 64 tokens all lie past M only stage data (few-token launches,
     // which take RT < 4; the 256-row form keeps a branch-free loop).
-    const bool live = RT == 4 || m0 + 64 * wm < M;
-    for (int b = 0; b < nblk; b += 2) {
+    // KS: every wave is live; the second half skips an odd block past the last.
+    const bool live = KS || RT == 4 || m0 + 64 * wm < M;
+    for (int b = 0; b < nst; b += 2) {
         gload(b + 2, r0);
-        if (live) compute(0);
+        if (live && (!KS || 2 * b + wm < nblk)) compute(0);
         lstore(1, r1);
         lds_barrier();
-        if (b + 1 < nblk) {
+        if (b + 1 < nst) {
             gload(b + 3, r1);
-            if (live) compute(1);
+            if (live && (!KS || 2 * b + 2 + wm < nblk)) compute(1);
             lstore(0, r0);
             lds_barrier();
         }
+    }
+    if constexpr (KS) {  // odd-block sums of wave (1, wn) join those of wave (0, wn)
+        uint32_t *red = reinterpret_cast<uint32_t *>(lds) + (wn * 64 + l) * 16 * RT;
+        if (wm == 1) {
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < RT; ++tj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        red[(ti * RT + tj) * 4 + e] = BLOCKED ? __float_as_uint(yacc[ti][tj][e])
+                                                              : (uint32_t)iacc[ti][tj][e];
+        }
+        __syncthreads();
+        if (wm == 1) return;
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < RT; ++tj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t o = red[(ti * RT + tj) * 4 + e];
+                    if (BLOCKED) yacc[ti][tj][e] += __uint_as_float(o);
+                    else iacc[ti][tj][e] += (int)o;
+                }
     }
 
     // epilogue: lane (g, j), tile (ti, tj), element e -> token m0+64wm+16ti+j,
     // row 16(T0+RT*wn+tj)+4g+e: four consecutive outputs of one token per store
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-        const int m = m0 + 64 * wm + 16 * ti + j;
+        const int m = m0 + (KS ? 0 : 64 * wm) + 16 * ti + j;
         if (m >= M) continue;
         // blocked: y = s_a * sum * 2^-6 (decoded weights are 64 t); SG 0: exact integer
         // sum times s_a * s_w
@@ -1392,8 +1437,16 @@ void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float 
         else
             hipLaunchKernelGGL((gemm_kernel<OUT, SG, 4>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
     }
-    else if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-    else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    else if constexpr (SG != 64) {  // up to 64 tokens: two blocks per stage
+        const bool ks = M <= 64;
+        if (rt == 2 && ks) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        else if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        else if (ks) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    } else {
+        if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    }
 }
 
 // Integer sums over all of K are held as 64 * sum in int32: |64 * 127 * K| < 2^31.
