@@ -631,12 +631,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // weights per scale (scales staged per block: [tile][16 rows] or
 // [tile][16 rows][2 halves]) or 0 (one scale: integer sums over all of K,
 // scaled once in the epilogue).
-// KS (at most 64 tokens, RT <= 2, SG 128 or 0): the token tile's second half
-// would hold no tokens, so each pipeline stage carries two blocks instead: LDS
-// rows 64..127 of the activation tile, and the brick and scale slots past the
-// first 4*RT tiles, hold the odd block for tokens 0..63.  Waves wm = 0 sum the
-// even blocks, wm = 1 the odd ones; the two partial sums are added once, through
-// LDS, before the epilogue (a fixed order, so results are deterministic).
+// KS (RT <= 2, SG 128 or 0): 64-token tiles, each pipeline stage carrying two
+// blocks: LDS rows 0..63 of the activation tile and the first 4*RT brick and
+// scale slots hold the even block, rows 64..127 and the next 4*RT slots the odd
+// one.  Waves wm = 0 sum the even blocks, wm = 1 the odd ones; the two partial
+// sums are added once, through LDS, before the epilogue (a fixed order, so
+// results are deterministic).  Half the blocks per workgroup and twice the
+// workgroups of the 128-token tiles, at twice the weight decoding.
 template <int OUT, int SG, int RT, bool KS = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                              const float *__restrict__ scales,
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
     int t = blockIdx.x;
     if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);  // XCD-aware order
     const int tm = t % ntm, tn = t / ntm;
-    const int m0 = tm * kGemmBM, T0 = tn * (4 * RT);  // RT row tiles per wave, 4 waves across
+    const int m0 = tm * (KS ? 64 : kGemmBM), T0 = tn * (4 * RT);  // RT row tiles per wave, 4 waves across
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, j = l & 15;
@@ -1425,27 +1426,57 @@ int gemm_row_tiles(int M, int N) {
     return 1;
 }
 
+// Launch plan of the prefill product.  With fewer than 256-row tiles, 64-token
+// tiles with two blocks per stage (KS) replace the 128-token ones when there
+// are at most 128 tokens or the 128-token grid would stay under 200 workgroups
+// (measured: 13824x2560 at 16 / 64 / 128 tokens 11.26 / 12.36 / 16.3 -> 9.36 /
+// 10.51 / 14.3 us, 2560x2560 at 128 tokens 14.9 -> 9.9 us, 512x2560x6912 35.2 ->
+// 31.8 us; at 256 tokens x 13824 rows, 216 workgroups already, 22.5 -> 25.2 us,
+// so the 128-token tiles stay there).  Not for 64-weight scales (their staging
+// fills the scale slots).
+struct GemmPlan {
+    int rt, ntm, ntn;
+    bool ks;
+};
+GemmPlan gemm_plan(int M, int N, int SG) {
+    GemmPlan g;
+    g.rt = gemm_row_tiles(M, N);
+    g.ntm = (M + kGemmBM - 1) / kGemmBM;
+    g.ntn = (N + 64 * g.rt - 1) / (64 * g.rt);
+    g.ks = g.rt < 4 && SG != 64 && (M <= 128 || (int64_t)g.ntm * g.ntn < 200);
+    if (g.ks) {
+        g.ntm = (M + 63) / 64;
+        g.rt = (int64_t)g.ntm * ((N + 127) / 128) >= 200 ? 2 : 1;
+        g.ntn = (N + 64 * g.rt - 1) / (64 * g.rt);
+    }
+    return g;
+}
+
 template <int OUT, int SG = 128>
 void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float *sa, void *y, int M, int N, int K,
                  hipStream_t st) {
-    const int ntm = (M + kGemmBM - 1) / kGemmBM, rt = gemm_row_tiles(M, N);
-    const int ntn = (N + 64 * rt - 1) / (64 * rt);
-    const dim3 grid(ntm * ntn), block(kGemmThreads);
-    if (rt == 4) {
+    const GemmPlan g = gemm_plan(M, N, SG);
+    const int ntm = g.ntm;
+    const dim3 grid(g.ntm * g.ntn), block(kGemmThreads);
+    if (g.rt == 4) {
         if constexpr (SG != 64)  // direct staging, in-wave interleaving
             hipLaunchKernelGGL((gemm_wide_kernel<OUT, SG>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
         else
             hipLaunchKernelGGL((gemm_kernel<OUT, SG, 4>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-    }
-    else if constexpr (SG != 64) {  // up to 64 tokens: two blocks per stage
-        const bool ks = M <= 64;
-        if (rt == 2 && ks) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-        else if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-        else if (ks) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-        else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+    } else if (g.rt == 2) {
+        if constexpr (SG != 64)
+            if (g.ks) {
+                hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+                return;
+            }
+        hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
     } else {
-        if (rt == 2) hipLaunchKernelGGL((gemm_kernel<OUT, SG, 2>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
-        else hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+        if constexpr (SG != 64)
+            if (g.ks) {
+                hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1, true>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
+                return;
+            }
+        hipLaunchKernelGGL((gemm_kernel<OUT, SG, 1>), grid, block, 0, st, p, s, q, sa, y, M, N, K, ntm);
     }
 }
 
@@ -1453,12 +1484,10 @@ void gemm_launch(const uint8_t *p, const float *s, const int8_t *q, const float 
 constexpr int kMaxIntK = 262144;
 
 // The launch's work-item count must fit the 32-bit grid size.
-bool gemm_grid_ok(int M, int N) {
-    const int rt = gemm_row_tiles(M, N);
-    const int64_t wgs = (int64_t)((M + kGemmBM - 1) / kGemmBM) * ((N + 64 * rt - 1) / (64 * rt));
-    return wgs * kGemmThreads < ((int64_t)1 << 32);
+bool gemm_grid_ok(int M, int N, int SG) {
+    const GemmPlan g = gemm_plan(M, N, SG);
+    return (int64_t)g.ntm * g.ntn * kGemmThreads < ((int64_t)1 << 32);
 }
-
 }  // namespace
 
 extern "C" {
@@ -1526,7 +1555,7 @@ bitnet_status_t bitnet_w2a8_gemm(const uint8_t *packed, const float *scales, con
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N, 128)) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (ydt == BITNET_DT_BF16) gemm_launch<0>(packed, scales, q, s_a, y, M, N, K, stream);
     else gemm_launch<1>(packed, scales, q, s_a, y, M, N, K, stream);
     return launched();
@@ -1555,7 +1584,7 @@ bitnet_status_t bitnet_w2a8_gemm_g(const uint8_t *packed, const float *scales, c
     if (!aligned(packed, 16) || !aligned(scales, 16) || !aligned(q, 16) || !aligned(s_a, 4) || !aligned(y, 16))
         return BITNET_ERR_INVALID_ARG;
     if (ydt != BITNET_DT_BF16 && ydt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N, scale_block)) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (scale_block == 0 && K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (scale_block == 64) {
         if (ydt == BITNET_DT_BF16) gemm_launch<0, 64>(packed, scales, q, s_a, y, M, N, K, stream);
@@ -1595,7 +1624,7 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
                                     hipStream_t stream) {
     if (!packed || !q || !acc || !aligned(packed, 16) || !aligned(q, 16) || !aligned(acc, 16))
         return BITNET_ERR_INVALID_ARG;
-    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N) || K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (!shape_ok(N, K) || M < 1 || !gemm_grid_ok(M, N, 128) || K > kMaxIntK) return BITNET_ERR_UNSUPPORTED_SHAPE;
     if (M <= kGemvMaxM) {
         GemvArgs a{packed, nullptr, q, nullptr, nullptr, acc, nullptr, nullptr, M, N, K, 0, 0, 0};
         gemv_launch<-1, true>(a, stream);

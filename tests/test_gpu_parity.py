@@ -329,10 +329,13 @@ def test_config4_gemm_full_sampled(gpu):
 # Few-token launches use narrower workgroup tiles (256 -> 128 -> 64 rows) so that the
 # grid still fills the chip: 64 x 13824 and 512 x 2560 take 64-row tiles, 256 x 13824
 # takes 128-row tiles, 512 x 13824 the full 256 rows.
-# up to 64 tokens: two blocks per pipeline stage, with 1 row tile per wave (64, 40 tokens) and
-# with 2 (26624 / 30736 rows: 208 / 241 workgroups of 128 rows), odd block counts included
+# 64-token tiles with two blocks per pipeline stage (up to 128 tokens, or few workgroups: 512 x
+# 2560 x 6912 runs 8 of them x 40 row groups), with 1 row tile per wave (64, 40, 130 tokens) and
+# with 2 (26624 / 30736 rows, and 100 tokens x 13824 rows), odd block counts and ragged token
+# tiles included; 256 tokens x 13824 rows keeps the 128-token tiles
 @pytest.mark.parametrize("M,N,K", [(64, 13824, 2560), (256, 13824, 2560), (512, 2560, 6912), (40, 2576, 640),
-                                   (48, 26624, 384), (17, 30736, 1152), (64, 26624, 2560)])
+                                   (48, 26624, 384), (17, 30736, 1152), (64, 26624, 2560), (100, 13824, 640),
+                                   (130, 2560, 1152)])
 def test_gemm_row_tile_choices_sampled(gpu, M, N, K):
     c = wl.small_case(M + N + K, M, N, K)
     p, st = pack_dev(c.T, c.S)
