@@ -437,6 +437,29 @@ def test_max_k_integer_sums_do_not_overflow(gpu):
     assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
 
 
+# ------------------------------------------------------------------ the largest grids
+# 2^20 rows (65,536 decode workgroups; 4,096 workgroups of the 256-row prefill kernel at 40
+# tokens), K of one and two blocks: sampled rows at both ends and in between
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (40, 128)])
+def test_tall_matrix_grids_sampled(gpu, M, K):
+    N = 1 << 20
+    r = wl.rng_for(131, M, K)
+    T = wl.ternary_uniform(r, N, K)
+    S = wl.uniform_scales(r, N, K)
+    xb = wl.normal_act(r, M, K)
+    p, st = pack_dev(T, S)
+    qd, sd = bn.bitnet_quant_act(x_dev(xb))
+    qo, so = oracle.quant_act_bf16(xb)
+    acc = host(bn.bitnet_w2a8_acc_i32(p, qd, N, K))
+    y = host(bn.bitnet_w2a8_gemv(p, st, qd, sd, N, K)) if M <= 16 else \
+        host(bn.bitnet_w2a8_gemm(p, st, qd, sd, N, K, out_dtype=torch.float32))
+    tiles = np.unique(np.concatenate([[0, 1, N // 32, N // 16 - 2, N // 16 - 1], r.choice(N // 16, 24)]))
+    rows = (tiles[:, None] * 16 + np.arange(16)).ravel()
+    ref = oracle.w2a8(oracle.pack_i2s(T[rows]), S[rows], qo, so, rows.size, K)
+    assert np.array_equal(acc[:, rows], ref["acc"])
+    assert_f32_close(y[:, rows], ref, f"tall {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ measurement helper
 @pytest.mark.parametrize("nbytes", [16, 4096 + 16, 10_011_152])
 def test_stream_read_probe_reads_every_word(gpu, nbytes):
