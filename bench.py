@@ -47,9 +47,9 @@ ROTATE_BYTES = 2 * LLC_BYTES
 # for a 64 MiB device copy (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000).  Valid only
 # for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha1": "9bdebb9bfecfe8de37c15607d19e988f937855bb",
-    "fused": {"bytes_per_launch": 10109720, "fetch_kib": 4911.5, "write_kib": 54.0},
-    "product": {"bytes_per_launch": 10076352, "fetch_kib": 4895.2, "write_kib": 54.0},
+    "kernel_source_sha1": "3b2ce980cabeeec7e00e5911f4725f975845f844",
+    "fused": {"bytes_per_launch": 10092671, "fetch_kib": 4903.0, "write_kib": 54.0},
+    "product": {"bytes_per_launch": 10076907, "fetch_kib": 4895.3, "write_kib": 54.0},
     "fetch_scale": 1.999, "write_scale": 1.000,
 }
 

@@ -138,13 +138,18 @@ __device__ __forceinline__ float max_abs8(const float f[8], float m) {
     return m;
 }
 
-// q = clamp(rint(x * inv), -127, 127) for 8 values, packed little-endian.
+// q = clamp(rint(x * inv), -127, 127) for 8 values, packed little-endian.  The
+// clamp never acts, so it is not executed: every x quantised has |x| <= amax_c
+// (amax is the exact maximum of the same fp32 values) and inv = 127 / amax_c is
+// correctly rounded, so |x * inv| <= 127 (1 + 2^-24)^2 rounds to at most 127 +
+// 2^-17 and rint gives at most 127 (8 fewer VALU operations per 8 values, which
+// the fused forms execute before requesting their weights: 20480x3200 step
+// 6.66 -> 6.39 us).
 __device__ __forceinline__ uint2 quantize8(const float f[8], float inv) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float r = rintf(__fmul_rn(f[i], inv));
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const float r = rintf(__fmul_rn(f[i], inv));
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)r;
         if (i < 4) lo |= b << (8 * i);
         else hi |= b << (8 * (i - 4));
