@@ -157,22 +157,27 @@ __device__ __forceinline__ uint2 quantize8(const float f[8], float inv) {
     return make_uint2(lo, hi);
 }
 
-// Max over the 64 lanes of a wave with DPP row operations (max is idempotent,
-// so mirrored / broadcast partners may repeat): after the row steps every lane
-// of a 16-lane row holds the row max, the two broadcasts fold rows 0..3 into
-// lane 63, which is then read as a scalar.
+// Max over the 64 lanes of a wave of non-negative floats (absolute values), with
+// DPP row operations on their bit patterns: for non-negative floats the unsigned
+// integer order is the float order, and an integer max needs no NaN
+// canonicalisation; with 0 (the identity of the unsigned max) for lanes a
+// broadcast does not reach, each step is one max with a DPP operand.  Max is
+// idempotent, so mirrored / broadcast partners may repeat: after the row steps
+// every lane of a 16-lane row holds the row max, the two broadcasts fold rows
+// 0..3 into lane 63, which is then read as a scalar.
 template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
-    v = fmaxf(v, dpp_f<0x142>(v));  // row_bcast:15
-    v = fmaxf(v, dpp_f<0x143>(v));  // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    uint32_t u = __float_as_uint(v);
+    u = max(u, dpp_u<0xB1>(u));   // quad_perm [1,0,3,2]
+    u = max(u, dpp_u<0x4E>(u));   // quad_perm [2,3,0,1]
+    u = max(u, dpp_u<0x141>(u));  // row_half_mirror
+    u = max(u, dpp_u<0x140>(u));  // row_mirror
+    u = max(u, dpp_u<0x142>(u));  // row_bcast:15
+    u = max(u, dpp_u<0x143>(u));  // row_bcast:31
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)u, 63));
 }
 
 // Workgroup barrier that waits only for this wave's LDS traffic: global loads
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
     constexpr int XM = AM < 0 ? 0 : AM;
     int *red = reinterpret_cast<int *>(smem);
     int8_t *qs = reinterpret_cast<int8_t *>(smem);
-    // LDS forms: after the q region, 16 dequant factors then [12 waves][4 tokens] partial amax
+    // LDS forms: after the q region, 16 dequant factors then [4 tokens][12 waves] partial amax
     float *tail = reinterpret_cast<float *>(smem + (LDSQ ? gemv_fused_region(M, K, nwc) : 0));
 
     if (FORM == kQuantWaves && w >= nwc) {
@@ -438,14 +443,23 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs args) {
                     for (int r = 0; r < CR; ++r)
                         if (l + kWave * r < nchw) mx = max_abs8(xf[m][r], mx);
                     mx = wave_max(mx);
-                    if (l == 0) amax_part[w * 4 + m] = mx;
+                    if (l == 0) amax_part[m * 12 + w] = mx;
+                    if (w == 0 && l >= nwc && l < 12) amax_part[m * 12 + l] = 0.0f;  // slots of no wave
                 }
                 lds_barrier();
 #pragma unroll
                 for (int m = 0; m < MW; ++m) {
                     if (m >= M) break;
                     float am = 0.0f;
-                    for (int ww = 0; ww < nwc; ++ww) am = fmaxf(am, amax_part[ww * 4 + m]);
+                    {  // the 12 wave slots of token m in one round trip (non-negative: integer max)
+                        const v4i *pv = reinterpret_cast<const v4i *>(amax_part + m * 12);
+                        const v4i p0 = pv[0], p1 = pv[1], p2 = pv[2];
+                        uint32_t u = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            u = max(u, max(max((uint32_t)p0[e], (uint32_t)p1[e]), (uint32_t)p2[e]));
+                        am = __uint_as_float(u);
+                    }
                     const float amax_c = fmaxf(am, 1e-5f);
                     const float inv = __fdiv_rn(127.0f, amax_c);
 #pragma unroll
