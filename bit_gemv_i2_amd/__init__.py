@@ -100,6 +100,15 @@ def lib():
     """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
     global _lib
     if _lib is None:
+        # The kernels must run on the HIP runtime that owns the device memory and
+        # streams passed in.  torch bundles its own libamdhip64 under the same
+        # soname; with torch loaded first the dynamic linker binds this library to
+        # that copy, while loading this library first would map the system runtime
+        # and torch would then load a second one beside it.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
                                "(run `python -m bit_gemv_i2_amd.build`)")

@@ -35,6 +35,25 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, s), s
 
 
+def test_one_hip_runtime_whatever_the_import_order():
+    """The library shares torch's HIP runtime even when it is loaded before torch
+    is imported (two runtimes in one process would own different memory and
+    streams).  Runs in fresh interpreters; no GPU call is made."""
+    import ast
+    import subprocess
+    import sys
+
+    pytest.importorskip("torch")
+    maps = "sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l})"
+    for first in ("import bit_gemv_i2_amd as bn; bn.lib(); import torch",
+                  "import torch; import bit_gemv_i2_amd as bn; bn.lib()"):
+        out = subprocess.run([sys.executable, "-c", f"{first}; print({maps})"], cwd=ROOT,
+                             capture_output=True, text=True, timeout=300)
+        assert out.returncode == 0, out.stderr
+        runtimes = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+        assert len(runtimes) == 1, (first, runtimes)
+
+
 def test_status_strings():
     assert bn.bitnet_status_str(0) == "ok"
     assert "invalid" in bn.bitnet_status_str(1)
