@@ -138,23 +138,33 @@ __device__ __forceinline__ float max_abs8(const float f[8], float m) {
     return m;
 }
 
-// q = clamp(rint(x * inv), -127, 127) for 8 values, packed little-endian.  The
-// clamp never acts, so it is not executed: every x quantised has |x| <= amax_c
+// q = clamp(rint(x * inv), -127, 127) for 8 values, packed little-endian.
+// The clamp never acts, so it is not executed: every x quantised has |x| <= amax_c
 // (amax is the exact maximum of the same fp32 values) and inv = 127 / amax_c is
 // correctly rounded, so |x * inv| <= 127 (1 + 2^-24)^2 rounds to at most 127 +
 // 2^-17 and rint gives at most 127 (8 fewer VALU operations per 8 values, which
 // the fused forms execute before requesting their weights: 20480x3200 step
 // 6.66 -> 6.39 us).
+// Rounding by one fp32 add: for |v| < 2^22, v + 1.5 * 2^23 lies in [2^23, 2^24),
+// where the spacing of floats is 1, so the add rounds v to an integer, half to
+// even (1.5 * 2^23 is even), and the sum's low mantissa byte is that integer in
+// two's complement.  v_perm gathers four such bytes per word.  The product is
+// rounded to fp32 first (no contraction into one fused multiply-add, whose single
+// rounding would decide ties of the exact product instead).  Checked against
+// rint on every fp32 value of magnitude below 127.5; it saves the rint and the
+// int conversion (fused 13824x2560 step 4.79 -> 4.73 us, 8 tokens 13.4 -> 12.9).
 __device__ __forceinline__ uint2 quantize8(const float f[8], float inv) {
-    uint32_t lo = 0, hi = 0;
+#pragma clang fp contract(off)
+    uint32_t u[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float r = rintf(__fmul_rn(f[i], inv));
-        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)r;
-        if (i < 4) lo |= b << (8 * i);
-        else hi |= b << (8 * (i - 4));
+        const float v = f[i] * inv;
+        u[i] = __float_as_uint(v + 12582912.0f);
     }
-    return make_uint2(lo, hi);
+    // perm(hi, lo, sel): selector bytes 0-3 take bytes of lo, 4-7 of hi, 0x0c gives zero
+    const uint32_t w0 = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u) | __builtin_amdgcn_perm(u[3], u[2], 0x04000c0cu);
+    const uint32_t w1 = __builtin_amdgcn_perm(u[5], u[4], 0x0c0c0400u) | __builtin_amdgcn_perm(u[7], u[6], 0x04000c0cu);
+    return make_uint2(w0, w1);
 }
 
 // Max over the 64 lanes of a wave of non-negative floats (absolute values), with
