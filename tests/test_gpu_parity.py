@@ -102,6 +102,51 @@ def test_quant_f32_and_edge_bitexact(gpu, M, K):
     assert np.all(host(q)[0] == 0)
 
 
+def tie_activations(M, K, seed):
+    """Activations whose every scaled value x * inv is an exact half-integer: even tokens
+    hold half-integers with amax 127 (inv = 1), odd tokens odd integers with amax 254
+    (inv = 0.5).  All are exact in bf16 as well as fp32."""
+    r = wl.rng_for(seed, M, K)
+    x = np.empty((M, K), np.float32)
+    for m in range(M):
+        if m % 2 == 0:
+            x[m] = r.integers(-127, 127, size=K) + 0.5
+            x[m, m % K] = 127.0
+        else:
+            x[m] = 2 * r.integers(-127, 127, size=K) + 1
+            x[m, m % K] = -254.0
+    return x
+
+
+# Round half to even on exact ties, in the standalone quantiser and in every fused form:
+# quantise-first (13824 rows), all waves (272 rows), busiest-SIMD split (2560 x 1280) and
+# the extra quant waves (8 tokens).
+@pytest.mark.parametrize("M,N,K", [(1, 13824, 2560), (2, 272, 2688), (1, 2560, 1280), (8, 2064, 2560)])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_quant_exact_ties_round_half_to_even(gpu, xdt, M, N, K):
+    x = tie_activations(M, K, 73)
+    if xdt == "bf16":
+        bits = wl.bf16_bits(x)
+        assert np.array_equal(wl.bf16_to_f32(bits), x)
+        xd = x_dev(bits)
+        qo, so = oracle.quant_act_bf16(bits)
+    else:
+        xd = dev(x)
+        qo, so = oracle.quant_act_f32(x)
+    ties = np.ones((M, K), bool)
+    ties[np.arange(M), np.arange(M) % K] = False
+    assert np.all(qo[ties] % 2 == 0) and np.all(np.abs(qo[~ties]) == 127)
+    q, s = bn.bitnet_quant_act(xd)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    c = wl.small_case(M * 7 + N + K, M, N, K)
+    p, st = pack_dev(c.T, c.S)
+    q_out = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_out = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = bn.bitnet_w2a8_gemv_act(p, st, xd, N, K, q_out=q_out, s_a_out=s_out)
+    assert np.array_equal(host(q_out), qo) and np.array_equal(host(s_out), so)
+    assert_f32_close(host(y), oracle_ref(c.T, c.S, qo, so), f"ties {xdt} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,H", [(1, 6912), (8, 6912), (3, 48)])
 def test_quant_fold_bitexact(gpu, M, H):
     y = wl.rng_for(52, M, H).standard_normal((M, 2 * H)).astype(np.float32) * 3
