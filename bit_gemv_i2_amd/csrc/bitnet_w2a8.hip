@@ -1736,9 +1736,13 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
                                                                    : in_dt;
         int nw, per;
         gemv_split(L.K, L.N, dev, &nw, &per);
-        // one launch when the cheap fused form applies, else quantise + multiply
-        // (the fused form re-quantises in every workgroup: worth it for one or two tokens)
-        const bool fused = M <= 2 && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
+        // One launch when the cheap fused form applies, else quantise + multiply.  The
+        // fused form re-quantises in every workgroup: worth it up to four tokens of a plain
+        // input, up to two behind a junction, whose two fp32 halves per token cost more
+        // (measured: 13824x2560 with fp32 input, 4 tokens 7.04 us against 7.11 us in two
+        // launches; 2560x6912 behind the fold, 3 tokens 9.35 us against 7.26 us).
+        const bool fused = (M <= 2 || (M <= 4 && L.fold_input == BITNET_JUNCTION_NONE)) && per <= 8 &&
+                           gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
                            gemv_fused_form(dt, M, L.K, L.N, dev) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};

@@ -294,8 +294,9 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
  * layer's input.  This is the chained decode of a BitNet model's linear layers
  * ([P2] "Architecture foundations": W2A8 products; [P3] "Why WASM": a 2.4B ternary
  * model), with the fused gate+up output brought to the down-projection width
- * by the linear fold or the squared-ReLU gate.  One launch per layer when M <= 2
- * (re-quantisation fused into the product), else two.
+ * by the linear fold or the squared-ReLU gate.  One launch per layer
+ * (re-quantisation fused into the product) when M <= 2, or M <= 4 for a layer
+ * without a junction in front; else two.
  * A fold_input outside 0..2 gives BITNET_ERR_INVALID_ARG.
  *   layers     host array of n descriptors (device pointers inside)
  *   x          device, [M][layers[0].K], xdt BITNET_DT_BF16 or BITNET_DT_F32

@@ -74,7 +74,7 @@ def test_chain_layer_local_parity(gpu, M, junction):
 
 
 @pytest.mark.parametrize("junction", JUNCTIONS)
-@pytest.mark.parametrize("M", [1, 2, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
 def test_chain_equals_products_called_one_by_one(gpu, M, junction):
     Ts, Ss, ws, folds = _small_chain(10 + M, junction)
     xb = wl.normal_act(wl.rng_for(73, M), M, SMALL[0][1])
