@@ -1737,12 +1737,17 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
         int nw, per;
         gemv_split(L.K, L.N, dev, &nw, &per);
         // One launch when the cheap fused form applies, else quantise + multiply.  The
-        // fused form re-quantises in every workgroup: worth it up to four tokens of a plain
-        // input, up to two behind a junction, whose two fp32 halves per token cost more
-        // (measured: 13824x2560 with fp32 input, 4 tokens 7.04 us against 7.11 us in two
-        // launches; 2560x6912 behind the fold, 3 tokens 9.35 us against 7.26 us).
-        const bool fused = (M <= 2 || (M <= 4 && L.fold_input == BITNET_JUNCTION_NONE)) && per <= 8 &&
-                           gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
+        // fused form re-quantises in every workgroup, so its cost grows with the tokens
+        // times the waves sharing each SIMD: worth it up to two tokens, and up to four on a
+        // plain input while tokens x waves stays within twice the device's wave slots
+        // (measured with fp32 input, fused against two launches: 13824x2560 at 3 tokens
+        // 6.56 against 7.03 us; 20480x3200 at 3 tokens 11.9 us, two launches about 8.5).
+        // Behind a junction the two fp32 halves per token cost more (2560x6912 behind the
+        // fold, 3 tokens: 9.35 against 7.26 us), so there it stays at two.
+        const int64_t grid_waves = (int64_t)(L.N / kTileN) * nw;
+        const bool few = M <= 2 || (M <= 4 && L.fold_input == BITNET_JUNCTION_NONE && dev.waves > 0 &&
+                                    M * grid_waves <= 2 * dev.waves);
+        const bool fused = few && per <= 8 && gemv_fused_lds(M, L.K, nw) <= kMaxLds &&
                            gemv_fused_form(dt, M, L.K, L.N, dev) == kAllWaves;
         if (fused) {
             GemvArgs a{L.packed, L.scales, in, nullptr, out, nullptr, nullptr, nullptr, M, L.N, L.K, 0, 0, 0};

@@ -296,7 +296,9 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
  * model), with the fused gate+up output brought to the down-projection width
  * by the linear fold or the squared-ReLU gate.  One launch per layer
  * (re-quantisation fused into the product) when M <= 2, or M <= 4 for a layer
- * without a junction in front; else two.
+ * without a junction in front whose grid is small against the device (M times
+ * its waves at most twice the device's wave slots); else two.  Results are the
+ * same either way.
  * A fold_input outside 0..2 gives BITNET_ERR_INVALID_ARG.
  *   layers     host array of n descriptors (device pointers inside)
  *   x          device, [M][layers[0].K], xdt BITNET_DT_BF16 or BITNET_DT_F32
