@@ -15,8 +15,9 @@ algorithmic bytes (packed weights + fp32 block scales + bf16 activations +
 fp32 outputs) over its average duration in the timed region (HIP events on the
 launch stream around the captured steps, one launch each); "product_kernel"
 gives the same for the product alone (int8 q in).  Beside them,
-"attainable_read" is what one bare pass of 16-byte loads over the same number
-of bytes achieves on this GPU, and "stream_ceiling_1GiB" what the same read
+"attainable_read" is what one bare pass of 16-byte non-temporal loads (the
+hint the product's weight loads carry) over the same number of bytes achieves
+on this GPU, and "stream_ceiling_1GiB" what the same read
 sustains over 1 GiB; "product_kernel_at_scale" gives the product and the fused
 step on a 262144x2560 matrix (189 MB a launch), where per-launch latency no
 longer dominates.
@@ -221,7 +222,7 @@ def attainable_read(torch, bn, nbytes, reps=10):
     us_noout = graph_us_per_launch(torch, lambda i: bn.bitnet_probe_stream_read(bufs[i % nrot], sink, 1), nrot, reps)
     del bufs
     torch.cuda.empty_cache()
-    return {"what": "one pass of 16-byte loads, one per thread, over the same number of bytes, each wave storing "
+    return {"what": "one pass of 16-byte non-temporal loads, one per thread, over the same number of bytes, each wave storing "
                     "one word (bitnet_probe_stream_read mode 0); no_output: the same read storing nothing (mode 1)",
             "bytes": n, "us": us, "GBps": n / us / 1e3, "no_output_us": us_noout, "no_output_GBps": n / us_noout / 1e3}
 
@@ -236,7 +237,7 @@ def stream_ceiling(torch, bn, reps=5):
     us = graph_us_per_launch(torch, lambda i: bn.bitnet_probe_stream_read(bufs[i % 2], sink, 0), 2, reps)
     del bufs, sink
     torch.cuda.empty_cache()
-    return {"what": "one-pass read of 1 GiB, 16-byte loads (bitnet_probe_stream_read mode 0)",
+    return {"what": "one-pass read of 1 GiB, 16-byte non-temporal loads (bitnet_probe_stream_read mode 0)",
             "bytes": n, "us": us, "GBps": n / us / 1e3}
 
 

@@ -503,7 +503,7 @@ class Chain:
 
 # ------------------------------------------------------------------ measurement helper
 def bitnet_probe_stream_read(src, sink=None, mode=0, stream=None):
-    """One plain pass of 16-byte loads over the device tensor `src` (not part of
+    """One pass of 16-byte non-temporal loads over the device tensor `src` (not part of
     the product path; the benchmark's attainable-bandwidth reference).  mode 0:
     returns the uint32 sink whose sum (mod 2^32) is the sum of src's 32-bit
     words; mode 1: no output (the read-only floor), the sink is left as it was."""

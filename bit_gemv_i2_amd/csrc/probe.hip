@@ -1,4 +1,4 @@
-// Measurement helper: one plain pass of 16-byte loads over a device buffer,
+// Measurement helper: one pass of 16-byte non-temporal loads over a device buffer,
 // the bandwidth a bare stream attains at a given size on this GPU.  The
 // benchmark prices the product kernels against it next to the published HBM
 // peak, because at a few MB a single launch cannot reach that peak (launch
@@ -8,6 +8,8 @@
 #include "bitnet_w2a8.h"
 
 namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kProbeThreads = 256;
 constexpr size_t kProbeMaxBlocks = 65536;
@@ -29,7 +31,8 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4 
     const size_t stride = (size_t)gridDim.x * kProbeThreads;
     uint32_t acc = 0;
     for (size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) {
-        const uint4 v = src[i];
+        // streaming (non-temporal) 16-byte loads, as the product's weight stream uses
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src + i));
         acc += v.x + v.y + v.z + v.w;
     }
     acc = dpp_add<0xB1, 0xF>(acc);   // quad_perm [1,0,3,2]

@@ -320,10 +320,10 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
 
 /* ---------------------------------------------------------------- measurement helper */
 
-/* Not part of the product path: one plain pass of 16-byte loads over `bytes`
- * of device memory, the bandwidth a bare stream attains at that size, against
- * which the benchmark prices the product kernels next to the published HBM
- * peak.  mode 0: every wave writes the wrapping 32-bit sum of the words it
+/* Not part of the product path: one pass of 16-byte non-temporal (streaming)
+ * loads over `bytes` of device memory, the bandwidth a bare stream attains at
+ * that size, against which the benchmark prices the product kernels next to
+ * the published HBM peak.  mode 0: every wave writes the wrapping 32-bit sum of the words it
  * read to one sink entry, so the sum of all entries (mod 2^32) is the sum of
  * every 32-bit word of the buffer; mode 1: a wave writes only if its sum equals
  * one fixed value (practically never) -- the floor of a read with no output,
