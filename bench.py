@@ -50,9 +50,9 @@ ROTATE_BYTES = 2 * LLC_BYTES
 # for a 64 MiB device copy (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000).  Valid only
 # for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha1": "7ad4b180491a07dd816c4adc00320d04335e1a86",
-    "fused": {"bytes_per_launch": 10104960, "fetch_kib": 4909.0, "write_kib": 54.0},
-    "product": {"bytes_per_launch": 10076299, "fetch_kib": 4895.0, "write_kib": 54.0},
+    "kernel_source_sha1": "6e91de8415553fc052f67f1b6c5595916af4366f",
+    "fused": {"bytes_per_launch": 10104986, "fetch_kib": 4909.0, "write_kib": 54.0},
+    "product": {"bytes_per_launch": 10076325, "fetch_kib": 4895.0, "write_kib": 54.0},
     "fetch_scale": 1.999, "write_scale": 1.000,
 }
 
