@@ -364,6 +364,39 @@ def format_shapes(torch, bn, wl, reps=10):
     return out
 
 
+def lut_shapes(torch, bn, wl, reps=10, tiles=(1, 2, 4)):
+    """The table-lookup decode product (bitnet_w2a8_gemv_lut, one token) beside the
+    matrix-core product on the same weight rotation, for the four decode shapes."""
+    out = []
+    cases = [("2560x2560", 1), ("13824x2560", 2), ("20480x3200", 3), ("2560x6912", None)]
+    for name, cfg in cases:
+        if cfg is None:
+            T, S = wl.stack_matrix(0, 5)
+            N, K = T.shape
+            xbits = wl.normal_act(wl.rng_for(5, 99), 1, K)
+        else:
+            cc = wl.CONFIGS[cfg](M=1)
+            T, S = (bn.bitnet_ternarize_absmean(cc.W) if cc.T is None else (cc.T, cc.S))
+            N, K, xbits = cc.N, cc.K, cc.x_bits
+        ds = DecodeShape(torch, bn, "lut_" + name, N, K, 1, T, S, xbits)
+        ds.quant(0)
+        n = ds.rot.R
+        r = {"shape": "lut_gemv_" + name, "M": 1, "N": N, "K": K, "rotation_copies": n,
+             "mfma_gemv_us": graph_us_per_launch(torch, ds.gemv, n, reps)}
+        for t in tiles:
+            def lut(i, t=t):
+                p, s = ds.rot[i]
+                bn.bitnet_w2a8_gemv_lut(p, s, ds.q, ds.sa, N, K, t, y=ds.y)
+            us = graph_us_per_launch(torch, lut, n, reps)
+            r[f"lut_us_tiles{t}"] = us
+            r[f"lut_packed_GBps_tiles{t}"] = N * K / 4 / us / 1e3
+        r["lut_over_mfma_best"] = min(r[f"lut_us_tiles{t}"] for t in tiles) / r["mfma_gemv_us"]
+        del ds
+        torch.cuda.empty_cache()
+        out.append(r)
+    return out
+
+
 def medium_batch_shapes(torch, bn, wl, reps=10):
     """13824x2560 between decode and prefill: the decode kernel up to M=16, the
     prefill kernel from M=16 to 128 (weights rotated through HBM for both)."""
@@ -488,6 +521,10 @@ def profile_run(torch, bn, wl):
     for i in range(64):
         d.fused(i)
     torch.cuda.synchronize()
+    for i in range(64):
+        p, s = d.rot[i]
+        bn.bitnet_w2a8_gemv_lut(p, s, d.q, d.sa, c.N, c.K, 2, y=d.y)
+    torch.cuda.synchronize()
     del d
     c4 = wl.config4()
     w4 = bn.PackedWeight.from_ternary(c4.T, c4.S)
@@ -497,7 +534,7 @@ def profile_run(torch, bn, wl):
     for i in range(16):
         w4.gemm(q4, s4, y=y4)
     torch.cuda.synchronize()
-    log(f"profile run done: copy {n} B x3, gemv x64, fused x64, prefill 512x13824x2560 x16")
+    log(f"profile run done: copy {n} B x3, gemv x64, fused x64, lut gemv x64, prefill 512x13824x2560 x16")
 
 
 def main():
@@ -628,7 +665,7 @@ def main():
         r = prefill_shape(torch, bn, wl)
         log(json.dumps(r))
         shapes.append(r)
-        for r in format_shapes(torch, bn, wl) + medium_batch_shapes(torch, bn, wl):
+        for r in format_shapes(torch, bn, wl) + medium_batch_shapes(torch, bn, wl) + lut_shapes(torch, bn, wl):
             log(json.dumps(r))
             shapes.append(r)
         for r in stack_shape(torch, bn, wl):

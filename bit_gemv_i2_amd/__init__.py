@@ -84,6 +84,7 @@ _SIGS = {
     "bitnet_w2a8_gemv_act": ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3
                              + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_acc_i32": ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_gemv_lut": ([ctypes.c_void_p] * 6 + [ctypes.c_int] * 3 + [ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_chain_workspace_bytes": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
     "bitnet_w2a8_chain": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
@@ -428,6 +429,24 @@ def bitnet_w2a8_acc_i32(packed, q, N: int, K: int, acc=None, stream=None):
     _ok(lib().bitnet_w2a8_acc_i32(_dev_ptr(packed, "packed"), _dev_ptr(q, "q"), _dev_ptr(acc, "acc"), M, N, K,
                                   _stream(stream)), "bitnet_w2a8_acc_i32")
     return acc
+
+
+def bitnet_w2a8_gemv_lut(packed, scales, q, s_a, N: int, K: int, tiles_per_group: int = 0, y=None, acc=None,
+                         with_acc: bool = False, stream=None):
+    """Table-lookup decode product for one token: y fp32 [1][N] (and, with
+    with_acc or a given acc, the exact int32 sums [1][N]).  Returns y, or (y, acc)."""
+    import torch
+    if q.dim() != 2 or q.shape[0] != 1:
+        raise ValueError("q must be int8 [1][K]")
+    if y is None:
+        y = torch.empty((1, N), dtype=torch.float32, device=q.device)
+    if acc is None and with_acc:
+        acc = torch.empty((1, N), dtype=torch.int32, device=q.device)
+    accp = _dev_ptr(acc, "acc") if acc is not None else None
+    _ok(lib().bitnet_w2a8_gemv_lut(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
+                                   _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), accp, N, K, tiles_per_group,
+                                   _stream(stream)), "bitnet_w2a8_gemv_lut")
+    return (y, acc) if acc is not None else y
 
 
 # ------------------------------------------------------------------ convenience

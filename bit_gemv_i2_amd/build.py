@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbitnet_w2a8.so")
-SOURCES = [os.path.join(CSRC, "bitnet_w2a8.hip"), os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "probe.hip")]
+SOURCES = [os.path.join(CSRC, "bitnet_w2a8.hip"), os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "probe.hip"),
+           os.path.join(CSRC, "gemv_lut.hip")]
 HEADERS = [os.path.join(INCLUDE, "bitnet_w2a8.h"), os.path.join(CSRC, "layout.h")]
 ARCH = "gfx950"
 

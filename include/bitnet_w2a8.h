@@ -318,6 +318,29 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
 bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int32_t *acc,
                                     int M, int N, int K, hipStream_t stream);
 
+/* Decode product for one token by table lookups, an experiment beside
+ * bitnet_w2a8_gemv (same operation, same operands).  The lookup-table idea is
+ * the CPU prior art of [P2] "5x performance leap: BitNet vs llama.cpp",
+ * "Architecture foundations", item 1 (TL1/TL2: precompute the sums a group of
+ * ternary weights can take against the activations, then look them up) and of
+ * [P3] "BitNet + WebAssembly" (16-entry table per weight group).  Here every
+ * pair of activations gets a 16-entry int16 table in LDS, indexed by the pair's
+ * two 2-bit codes as they sit in one nibble of the tile layout.
+ *   packed  device, tile layout, bitnet_packed_bytes(N,K) bytes
+ *   scales  device, tiled scales, bitnet_scale_count(N,K) fp32
+ *   q       device, int8 [K] (one token);  s_a device, fp32 [1]
+ *   y       device, fp32 [N] (out)
+ *   acc     device, int32 [N] (out: the exact sums over k of T[n][k] * Q[k]), or NULL
+ *   tiles_per_group  16-row tiles each workgroup covers (1, 2 or 4; 0 = 1): more
+ *           tiles amortise the table build over more weights
+ * Rules: the shape rules and K <= 2^22 (else UNSUPPORTED_SHAPE); other
+ * tiles_per_group values are INVALID_ARG.  y agrees with the exact value within
+ * 1e-5 of max(|y|, s_a * sum_b |S*A|); for a given shape and tiles_per_group the
+ * summation order, and so y, is fixed. */
+bitnet_status_t bitnet_w2a8_gemv_lut(const uint8_t *packed, const float *scales, const int8_t *q,
+                                     const float *s_a, float *y, int32_t *acc, int N, int K,
+                                     int tiles_per_group, hipStream_t stream);
+
 /* ---------------------------------------------------------------- measurement helper */
 
 /* Not part of the product path: one pass of 16-byte non-temporal (streaming)

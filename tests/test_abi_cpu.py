@@ -249,6 +249,22 @@ def test_gemm_acc_quant_validation():
     assert L.bitnet_quant_act_fold(_NULL, 1, 32, _FAKE, _FAKE, _NULL) == bn.BITNET_ERR_INVALID_ARG
 
 
+def test_lut_gemv_validation():
+    L = bn.lib()
+    f = L.bitnet_w2a8_gemv_lut
+    assert f(_NULL, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 2560, 2560, 0, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert f(_FAKE, _FAKE, _FAKE, _FAKE, _NULL, _FAKE, 2560, 2560, 0, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert f(_MIS, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 2560, 2560, 0, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert f(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, ctypes.c_void_p(0x100002), 2560, 2560, 1, _NULL) == \
+        bn.BITNET_ERR_INVALID_ARG
+    for tiles in (3, 8, -1):
+        assert f(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 2560, 2560, tiles, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert f(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 2560, 2500, 0, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert f(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 2568, 2560, 0, _NULL) == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert f(_FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, 16, (1 << 22) + 128, 0, _NULL) == \
+        bn.BITNET_ERR_UNSUPPORTED_SHAPE
+
+
 def test_product_path_has_no_fallback(monkeypatch):
     # a missing library must raise, never compute on the CPU
     monkeypatch.setattr(bn, "_lib", None)
