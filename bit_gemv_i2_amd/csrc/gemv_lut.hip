@@ -200,8 +200,10 @@ extern "C" bitnet_status_t bitnet_w2a8_gemv_lut(const uint8_t *packed, const flo
     if (tiles_per_group != 0 && tiles_per_group != 1 && tiles_per_group != 2 && tiles_per_group != 4)
         return BITNET_ERR_INVALID_ARG;
     if (bitnet_check_shape(N, K) != BITNET_OK || K > (1 << 22)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    // default: two tiles per workgroup while that still leaves one workgroup per CU
+    // (256 CUs; measured best at 13824 and 20480 rows), else one (2560 rows)
     int R = tiles_per_group;
-    if (R == 0) R = 1;
+    if (R == 0) R = (N >> 5) >= 256 ? 2 : 1;
     switch (R) {
         case 1: lut_launch<1>(packed, scales, q, s_a, y, acc, N, K, stream); break;
         case 2: lut_launch<2>(packed, scales, q, s_a, y, acc, N, K, stream); break;

@@ -331,8 +331,9 @@ bitnet_status_t bitnet_w2a8_acc_i32(const uint8_t *packed, const int8_t *q, int3
  *   q       device, int8 [K] (one token);  s_a device, fp32 [1]
  *   y       device, fp32 [N] (out)
  *   acc     device, int32 [N] (out: the exact sums over k of T[n][k] * Q[k]), or NULL
- *   tiles_per_group  16-row tiles each workgroup covers (1, 2 or 4; 0 = 1): more
- *           tiles amortise the table build over more weights
+ *   tiles_per_group  16-row tiles each workgroup covers (1, 2 or 4; 0 = 2 when that
+ *           leaves at least 256 workgroups, else 1): more tiles amortise the table
+ *           build over more weights, fewer leave more workgroups to fill the chip
  * Rules: the shape rules and K <= 2^22 (else UNSUPPORTED_SHAPE); other
  * tiles_per_group values are INVALID_ARG.  y agrees with the exact value within
  * 1e-5 of max(|y|, s_a * sum_b |S*A|); for a given shape and tiles_per_group the
