@@ -1,9 +1,12 @@
 """The library's offline host code (pack.cpp: ternarise, pack, repack, unpack)
-under the address + undefined-behaviour and the thread sanitizers.
+under the address + undefined-behaviour and the thread sanitizers, and the CPU
+oracle (oracle/oracle.c) under the address + undefined-behaviour sanitizers.
 
 tests/host/pack_sanitize.cpp drives round trips over many shapes and all three
-scale granularities; it is built here with g++ (host code only, no device code)
-and must run clean.  CPU only."""
+scale granularities; tests/host/oracle_sanitize.c calls every oracle function on
+exactly sized heap buffers and checks its products against a dense integer
+product.  Both are built here with the host compilers (no device code) and must
+run clean.  CPU only."""
 import os
 import shutil
 import subprocess
@@ -35,3 +38,24 @@ def test_pack_code_runs_clean_under_sanitizers(tmp_path, sanitizers):
     assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
     assert "ok (0 failures)" in run.stdout
     assert "runtime error" not in run.stderr and "WARNING: ThreadSanitizer" not in run.stderr
+
+
+ORACLE_DRIVER = os.path.join(ROOT, "tests", "host", "oracle_sanitize.c")
+ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+
+def test_oracle_runs_clean_under_address_and_undefined_sanitizers(tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "oracle_sanitize")
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fsanitize=address,undefined",
+           "-fno-omit-frame-pointer", ORACLE_DRIVER, ORACLE_SRC, "-o", exe, "-lm"]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    if build.returncode != 0 and "cannot find" in build.stderr and "san" in build.stderr:
+        pytest.skip("sanitizer runtime not installed")
+    assert build.returncode == 0, build.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
+    assert "ok (0 failures)" in run.stdout
+    assert "runtime error" not in run.stderr

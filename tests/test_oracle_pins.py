@@ -256,6 +256,131 @@ def test_scale_magnitude_bounds_value():
     assert np.array_equal(r["y"], r["y64"].astype(np.float32))
 
 
+# The tolerance magnitude mag = s_a * sum_b |S[n,b] * A[m,n,b]| (one absolute
+# value per 128-weight block: [P3] "What i2_s actually is", one float scale per
+# block, so the block sum A is the unit the scale multiplies).  Every fp32 / bf16
+# parity bound is 1e-5 * max(|y|, mag), so mag is pinned exactly, not only from
+# below: a per-weight magnitude, a wrong factor or a dropped block fails here.
+def _block_sums(T, Q):
+    """A[m, n, b] = sum over block b of T[n, k] * Q[m, k]: a dense int64 product per block."""
+    N, K = T.shape
+    B = K // 128
+    return np.einsum("nbk,mbk->mnb", T.astype(np.int64).reshape(N, B, 128),
+                     Q.astype(np.int64).reshape(Q.shape[0], B, 128))
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 16, 128, 1), (3, 48, 640, 2), (8, 64, 2560, 3)])
+def test_mag_is_sum_of_block_magnitudes_exactly(M, N, K, seed):
+    # unit scales and s_a = 1: mag = sum_b |A_b| exactly (integers below 2^53)
+    c = wl.small_case(seed, M, N, K, skind="ones")
+    q, _ = oracle.quant_act_bf16(c.x_bits)
+    r = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, np.ones(M, np.float32), N, K)
+    A = _block_sums(c.T, q)
+    want = np.abs(A).sum(axis=2)
+    assert np.array_equal(r["mag"], want.astype(np.float64))
+    # the data exercise the difference between the candidate definitions
+    per_weight = np.abs(q.astype(np.int64)) @ np.abs(c.T.astype(np.int64)).T
+    assert np.all(per_weight >= want) and np.any(per_weight > want)
+    if K > 128:
+        assert np.any(want > np.abs(A.sum(axis=2)))  # blocks of opposite sign cancel in y, not in mag
+
+
+def test_mag_with_scales_matches_exact_rational():
+    M, N, K = 2, 32, 1280
+    c = wl.small_case(7, M, N, K)
+    q, s = oracle.quant_act_bf16(c.x_bits)
+    r = oracle.w2a8(oracle.pack_i2s(c.T), c.S, q, s, N, K)
+    A = _block_sums(c.T, q)
+    B = K // 128
+    for m in range(M):
+        for n in range(0, N, 3):
+            exact = Fraction(float(s[m])) * sum(abs(Fraction(float(c.S[n, b])) * int(A[m, n, b])) for b in range(B))
+            assert abs(Fraction(r["mag"][m, n]) - exact) <= exact * Fraction(2 * B, 2 ** 53)
+
+
+def test_mag_closed_forms():
+    K, B = 512, 4
+    rng = wl.rng_for(31)
+    q = rng.integers(1, 128, size=(1, K)).astype(np.int8)  # positive activations
+    S = rng.uniform(0.5, 2.0, size=(3, B)).astype(np.float32)
+    T = np.zeros((3, K), np.int8)
+    T[0, 300] = -1                  # one nonzero weight: mag = |y|
+    T[1, :] = 1                     # every block positive: mag = y
+    T[2, :128] = 1                  # block 0 positive, block 1 negative: mag = |t0| + |t1|
+    T[2, 128:256] = -1
+    s_a = np.array([0.75], np.float32)
+    r = oracle.w2a8(oracle.pack_i2s(T), S, q, s_a, 3, K)
+    assert r["mag"][0, 0] == abs(r["y64"][0, 0]) and r["y64"][0, 0] < 0
+    assert r["mag"][0, 1] == r["y64"][0, 1] > 0
+    A = _block_sums(T, q)[0]
+    t0 = Fraction(float(S[2, 0])) * int(A[2, 0])
+    t1 = Fraction(float(S[2, 1])) * int(A[2, 1])
+    assert t0 > 0 > t1
+    assert Fraction(r["mag"][0, 2]) == Fraction(3, 4) * (abs(t0) + abs(t1))
+    assert Fraction(r["y64"][0, 2]) == Fraction(3, 4) * (t0 + t1)
+
+
+# Ties of the activation quantiser (reading R6: round half to even).  With
+# amax = 127 the factor 127/amax is exactly 1, with amax = 254 exactly 1/2, so
+# half-integers and odd integers / 2 land exactly on ties; numpy's rint rounds
+# half to even, round-half-away-from-zero differs at 62.5, -62.5, 0.5, ...
+def _tie_tokens():
+    half = np.arange(-126.5, 127.0, 1.0, dtype=np.float32)          # 254 exact ties at inv = 1
+    t1 = np.concatenate([[127.0, 0.0], half]).astype(np.float32)   # amax 127
+    odd = np.arange(-253.0, 254.0, 2.0, dtype=np.float32)           # 254 exact ties at inv = 1/2
+    t2 = np.concatenate([[254.0, 0.0], odd]).astype(np.float32)    # amax 254
+    return np.stack([t1, t2])
+
+
+def _expect_half_even(x):
+    inv = (np.float32(127) / np.abs(x).max(axis=1)).astype(np.float32)
+    assert inv[0] == 1.0 and inv[1] == 0.5
+    return np.rint(x.astype(np.float64) * inv[:, None].astype(np.float64)).astype(np.int8)
+
+
+def _check_tie_codes(q, x):
+    want = _expect_half_even(x)
+    assert np.array_equal(q, want)
+    row = list(x[0])
+    for v, code in [(62.5, 62), (-62.5, -62), (63.5, 64), (0.5, 0), (-0.5, 0), (1.5, 2), (126.5, 126)]:
+        assert q[0, row.index(np.float32(v))] == code, v
+    row = list(x[1])
+    for v, code in [(125.0, 62), (-125.0, -62), (127.0, 64), (1.0, 0), (253.0, 126)]:
+        assert q[1, row.index(np.float32(v))] == code, v
+
+
+def test_quant_ties_round_half_to_even():
+    x = _tie_tokens()
+    q, s = oracle.quant_act_f32(x)
+    _check_tie_codes(q, x)
+    assert s[0] == np.float32(1.0) and s[1] == np.float32(2.0)
+    # the same ties from bf16 inputs (every value above is exact in bf16)
+    xb = wl.bf16_bits(x)
+    assert np.array_equal(wl.bf16_to_f32(xb), x)
+    qb, sb = oracle.quant_act_bf16(xb)
+    assert np.array_equal(qb, q) and np.array_equal(sb, s)
+
+
+def test_fold_quant_ties_round_half_to_even():
+    x = _tie_tokens()
+    lo = np.floor(x).astype(np.float32)        # h = lo + hi rebuilds x exactly
+    hi = (x - lo).astype(np.float32)
+    q, s = oracle.fold_quant(np.concatenate([lo, hi], axis=1))
+    _check_tie_codes(q, x)
+    q2, _ = oracle.fold_quant(np.concatenate([hi, lo], axis=1))  # the sum is symmetric
+    assert np.array_equal(q2, q)
+
+
+def test_glu_quant_ties_round_half_to_even():
+    x = _tie_tokens()
+    ones = np.ones_like(x)
+    q, s = oracle.glu_quant(np.concatenate([ones, x], axis=1))          # relu(1)^2 * up = up
+    _check_tie_codes(q, x)
+    q4, s4 = oracle.glu_quant(np.concatenate([2 * ones, x / 4], axis=1))  # 4 * (up / 4), exact
+    _check_tie_codes(q4, x)
+    assert np.array_equal(s4, s)
+
+
 # --------------------------------------------------------------------------- #
 # absmean ternarisation
 # --------------------------------------------------------------------------- #
