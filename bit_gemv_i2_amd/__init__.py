@@ -139,6 +139,45 @@ def _dev_ptr(t, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _check(t, name: str, dtype, numel: int | None = None, shape: tuple | None = None):
+    """Raises ValueError unless tensor t has the given dtype and exactly `numel`
+    elements (or exactly `shape`).  Runs on metadata only, before any pointer is
+    taken or any launch is made: a buffer whose size disagrees with the library's
+    size authorities (bitnet_packed_bytes, bitnet_scale_count[_g], M*K, M*N) is
+    never handed to a kernel."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, not {t.numel()}")
+
+
+def _check_weights(packed, scales, N: int, K: int, scale_block: int = 128):
+    """packed / scales against bitnet_packed_bytes and bitnet_scale_count[_g]."""
+    import torch
+    nb = bitnet_packed_bytes(N, K)
+    ns = bitnet_scale_count(N, K) if scale_block == 128 else bitnet_scale_count_g(N, K, scale_block)
+    if nb == 0 or ns == 0:
+        raise BitnetError(BITNET_ERR_UNSUPPORTED_SHAPE if nb == 0 else BITNET_ERR_INVALID_ARG,
+                          f"weights of shape {N} x {K} (scale_block {scale_block})")
+    _check(packed, "packed", torch.uint8, numel=nb)
+    if scales is not None:
+        _check(scales, "scales", torch.float32, numel=ns)
+
+
+def _check_acts(q, s_a, K: int):
+    """q int8 [M][K] and s_a fp32 [M]; returns M."""
+    import torch
+    if q.dim() != 2 or q.shape[1] != K:
+        raise ValueError(f"q must be [M][{K}], not {tuple(q.shape)}")
+    _check(q, "q", torch.int8)
+    M = q.shape[0]
+    if s_a is not None:
+        _check(s_a, "s_a", torch.float32, numel=M)
+    return M
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -306,6 +345,8 @@ def bitnet_quant_act(x, q=None, s_a=None, stream=None):
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if s_a is None:
         s_a = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(q, "q", torch.int8, numel=M * K)
+    _check(s_a, "s_a", torch.float32, numel=M)
     _ok(lib().bitnet_quant_act(_dev_ptr(x, "x"), xdt, M, K, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"),
                                _stream(stream)), "bitnet_quant_act")
     return q, s_a
@@ -321,6 +362,8 @@ def _quant_two_half(name, y, q, s_a, stream):
         q = torch.empty((M, H), dtype=torch.int8, device=y.device)
     if s_a is None:
         s_a = torch.empty((M,), dtype=torch.float32, device=y.device)
+    _check(q, "q", torch.int8, numel=M * H)
+    _check(s_a, "s_a", torch.float32, numel=M)
     _ok(getattr(lib(), name)(_dev_ptr(y, "y"), M, H, _dev_ptr(q, "q"), _dev_ptr(s_a, "s_a"), _stream(stream)), name)
     return q, s_a
 
@@ -338,9 +381,11 @@ def bitnet_quant_act_relu2_glu(y, q=None, s_a=None, stream=None):
 def bitnet_w2a8_gemv(packed, scales, q, s_a, N: int, K: int, y=None, stream=None):
     """Decode product (M <= 16): y fp32 [M][N]."""
     import torch
-    M = q.shape[0]
+    _check_weights(packed, scales, N, K)
+    M = _check_acts(q, s_a, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    _check(y, "y", torch.float32, numel=M * N)
     _ok(lib().bitnet_w2a8_gemv(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), M, N, K, _stream(stream)),
         "bitnet_w2a8_gemv")
@@ -364,8 +409,14 @@ def bitnet_w2a8_gemv_act(packed, scales, x, N: int, K: int, fold: bool = False, 
         xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
         if xdt is None or x.shape[1] != K:
             raise ValueError("x must be bf16 or fp32 [M][K]")
+    _check_weights(packed, scales, N, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(y, "y", torch.float32, numel=M * N)
+    if q_out is not None:
+        _check(q_out, "q_out", torch.int8, numel=M * K)
+    if s_a_out is not None:
+        _check(s_a_out, "s_a_out", torch.float32, numel=M)
     qp = None if q_out is None else _dev_ptr(q_out, "q_out")
     sp = None if s_a_out is None else _dev_ptr(s_a_out, "s_a_out")
     _ok(lib().bitnet_w2a8_gemv_act(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"), xdt,
@@ -376,7 +427,8 @@ def bitnet_w2a8_gemv_act(packed, scales, x, N: int, K: int, fold: bool = False, 
 def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=None, stream=None):
     """Prefill product (any M): y [M][N] in bf16 (default) or fp32."""
     import torch
-    M = q.shape[0]
+    _check_weights(packed, scales, N, K)
+    M = _check_acts(q, s_a, K)
     if out_dtype is None:
         out_dtype = torch.bfloat16 if y is None else y.dtype
     ydt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(out_dtype)
@@ -384,6 +436,7 @@ def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=N
         raise ValueError("out_dtype must be bf16 or fp32")
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    _check(y, "y", out_dtype, numel=M * N)
     _ok(lib().bitnet_w2a8_gemm(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), ydt, M, N, K, _stream(stream)),
         "bitnet_w2a8_gemm")
@@ -393,9 +446,11 @@ def bitnet_w2a8_gemm(packed, scales, q, s_a, N: int, K: int, out_dtype=None, y=N
 def bitnet_w2a8_gemv_g(packed, scales, q, s_a, N: int, K: int, scale_block: int, y=None, stream=None):
     """Decode product at scale granularity scale_block (tiled scales of bitnet_pack_i2s_g)."""
     import torch
-    M = q.shape[0]
+    _check_weights(packed, scales, N, K, scale_block)
+    M = _check_acts(q, s_a, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    _check(y, "y", torch.float32, numel=M * N)
     _ok(lib().bitnet_w2a8_gemv_g(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                  _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), M, N, K, scale_block, _stream(stream)),
         "bitnet_w2a8_gemv_g")
@@ -406,7 +461,8 @@ def bitnet_w2a8_gemm_g(packed, scales, q, s_a, N: int, K: int, scale_block: int,
                        stream=None):
     """Prefill product at scale granularity scale_block."""
     import torch
-    M = q.shape[0]
+    _check_weights(packed, scales, N, K, scale_block)
+    M = _check_acts(q, s_a, K)
     if out_dtype is None:
         out_dtype = torch.bfloat16 if y is None else y.dtype
     ydt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(out_dtype)
@@ -414,6 +470,7 @@ def bitnet_w2a8_gemm_g(packed, scales, q, s_a, N: int, K: int, scale_block: int,
         raise ValueError("out_dtype must be bf16 or fp32")
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    _check(y, "y", out_dtype, numel=M * N)
     _ok(lib().bitnet_w2a8_gemm_g(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                  _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), ydt, M, N, K, scale_block,
                                  _stream(stream)), "bitnet_w2a8_gemm_g")
@@ -423,9 +480,11 @@ def bitnet_w2a8_gemm_g(packed, scales, q, s_a, N: int, K: int, scale_block: int,
 def bitnet_w2a8_acc_i32(packed, q, N: int, K: int, acc=None, stream=None):
     """Exact int32 product acc [M][N] through the decode (M <= 16) or prefill kernel."""
     import torch
-    M = q.shape[0]
+    _check_weights(packed, None, N, K)
+    M = _check_acts(q, None, K)
     if acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
+    _check(acc, "acc", torch.int32, numel=M * N)
     _ok(lib().bitnet_w2a8_acc_i32(_dev_ptr(packed, "packed"), _dev_ptr(q, "q"), _dev_ptr(acc, "acc"), M, N, K,
                                   _stream(stream)), "bitnet_w2a8_acc_i32")
     return acc
@@ -438,10 +497,15 @@ def bitnet_w2a8_gemv_lut(packed, scales, q, s_a, N: int, K: int, tiles_per_group
     import torch
     if q.dim() != 2 or q.shape[0] != 1:
         raise ValueError("q must be int8 [1][K]")
+    _check_weights(packed, scales, N, K)
+    _check_acts(q, s_a, K)
     if y is None:
         y = torch.empty((1, N), dtype=torch.float32, device=q.device)
     if acc is None and with_acc:
         acc = torch.empty((1, N), dtype=torch.int32, device=q.device)
+    _check(y, "y", torch.float32, numel=N)
+    if acc is not None:
+        _check(acc, "acc", torch.int32, numel=N)
     accp = _dev_ptr(acc, "acc") if acc is not None else None
     _ok(lib().bitnet_w2a8_gemv_lut(_dev_ptr(packed, "packed"), _dev_ptr(scales, "scales"), _dev_ptr(q, "q"),
                                    _dev_ptr(s_a, "s_a"), _dev_ptr(y, "y"), accp, N, K, tiles_per_group,
@@ -511,8 +575,11 @@ class Chain:
         xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
         if xdt is None:
             raise ValueError("x must be bf16 or fp32")
+        if x.dim() != 2 or x.shape[1] != self.weights[0].K:
+            raise ValueError(f"x must be [M][{self.weights[0].K}], not {tuple(x.shape)}")
         if y is None:
             y = torch.empty((M, self.weights[-1].N), dtype=torch.float32, device=x.device)
+        _check(y, "y", torch.float32, numel=M * self.weights[-1].N)
         ws = self.workspace(M, x.device)
         _ok(lib().bitnet_w2a8_chain(ctypes.cast(self._arr, ctypes.c_void_p), len(self.weights), _dev_ptr(x, "x"), xdt,
                                     M, _dev_ptr(y, "y"), _dev_ptr(ws, "workspace"), ws.numel(), _stream(stream)),
@@ -531,6 +598,9 @@ def bitnet_probe_stream_read(src, sink=None, mode=0, stream=None):
     nsink = lib().bitnet_probe_stream_read_sink_len(nbytes)
     if sink is None:
         sink = torch.empty((nsink,), dtype=torch.int32, device=src.device)
+    _check(sink, "sink", torch.int32)
+    if sink.numel() < nsink:
+        raise ValueError(f"sink must hold at least {nsink} entries, not {sink.numel()}")
     _ok(lib().bitnet_probe_stream_read(_dev_ptr(src, "src"), nbytes, _dev_ptr(sink, "sink"), sink.numel(), int(mode),
                                        _stream(stream)), "bitnet_probe_stream_read")
     return sink

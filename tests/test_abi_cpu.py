@@ -338,3 +338,98 @@ def test_g_variants_reject_bad_scale_block():
             bn.BITNET_ERR_INVALID_ARG
         assert bn.lib().bitnet_w2a8_gemm_g(None, None, None, None, None, 0, 1, 16, 128, sb, None) == \
             bn.BITNET_ERR_INVALID_ARG
+
+
+# Every device wrapper checks its tensors against the library's size authorities
+# (bitnet_packed_bytes, bitnet_scale_count[_g], M*K, M*N) before it takes a pointer:
+# a mis-sized buffer raises here, on host tensors, long before any launch could read or
+# write past it ([P4] "Matrix memory bounds and stride safety").
+def _operands(torch, M=2, N=48, K=384, G=128):
+    ns = bn.bitnet_scale_count(N, K) if G == 128 else bn.bitnet_scale_count_g(N, K, G)
+    return dict(packed=torch.zeros(bn.bitnet_packed_bytes(N, K), dtype=torch.uint8),
+                scales=torch.zeros(ns, dtype=torch.float32),
+                q=torch.zeros((M, K), dtype=torch.int8), s_a=torch.zeros(M, dtype=torch.float32),
+                y=torch.zeros((M, N), dtype=torch.float32), M=M, N=N, K=K)
+
+
+def _calls(torch, o):
+    N, K = o["N"], o["K"]
+    return {
+        "gemv": lambda **k: bn.bitnet_w2a8_gemv(k["packed"], k["scales"], k["q"], k["s_a"], N, K, y=k["y"]),
+        "gemm": lambda **k: bn.bitnet_w2a8_gemm(k["packed"], k["scales"], k["q"], k["s_a"], N, K, y=k["y"]),
+        "gemv_g": lambda **k: bn.bitnet_w2a8_gemv_g(k["packed"], k["scales"], k["q"], k["s_a"], N, K, 128, y=k["y"]),
+        "gemm_g": lambda **k: bn.bitnet_w2a8_gemm_g(k["packed"], k["scales"], k["q"], k["s_a"], N, K, 128, y=k["y"]),
+        "acc": lambda **k: bn.bitnet_w2a8_acc_i32(k["packed"], k["q"], N, K,
+                                                   acc=torch.zeros((k["q"].shape[0], N), dtype=torch.int32)),
+    }
+
+
+@pytest.mark.parametrize("which", ["gemv", "gemm", "gemv_g", "gemm_g", "acc"])
+def test_wrappers_reject_mis_sized_operands_before_any_launch(which):
+    torch = pytest.importorskip("torch")
+    o = _operands(torch)
+    call = _calls(torch, o)[which]
+    args = {k: o[k] for k in ("packed", "scales", "q", "s_a", "y")}
+    # correct sizes pass every check and stop only at the device test
+    with pytest.raises(ValueError, match="device tensor"):
+        call(**args)
+    bad = {
+        "packed": torch.zeros(o["packed"].numel() - 16, dtype=torch.uint8),
+        "scales": torch.zeros(o["scales"].numel() + 1, dtype=torch.float32),
+        "q": torch.zeros((o["M"], o["K"] - 128), dtype=torch.int8),
+        "s_a": torch.zeros(o["M"] + 1, dtype=torch.float32),
+        "y": torch.zeros((o["M"], o["N"] - 16), dtype=torch.float32),
+    }
+    wrong_dtype = {"packed": torch.zeros(o["packed"].numel(), dtype=torch.int8),
+                   "q": torch.zeros((o["M"], o["K"]), dtype=torch.uint8),
+                   "y": torch.zeros((o["M"], o["N"]), dtype=torch.float64)}
+    for name, t in list(bad.items()) + list(wrong_dtype.items()):
+        if which == "acc" and name in ("scales", "s_a", "y"):
+            continue
+        with pytest.raises(ValueError, match=name if name != "q" else "q"):
+            call(**dict(args, **{name: t}))
+    if which == "acc":
+        with pytest.raises(ValueError, match="acc"):
+            bn.bitnet_w2a8_acc_i32(o["packed"], o["q"], o["N"], o["K"],
+                                   acc=torch.zeros((o["M"], o["N"] + 16), dtype=torch.int32))
+
+
+def test_wrappers_reject_unsupported_weight_shapes_and_formats():
+    torch = pytest.importorskip("torch")
+    o = _operands(torch)
+    with pytest.raises(bn.BitnetError) as ei:    # N not a multiple of 16
+        bn.bitnet_w2a8_gemv(o["packed"], o["scales"], o["q"], o["s_a"], 40, o["K"])
+    assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(bn.BitnetError) as ei:    # no such scale granularity
+        bn.bitnet_w2a8_gemv_g(o["packed"], o["scales"], o["q"], o["s_a"], o["N"], o["K"], 32)
+    assert ei.value.status == bn.BITNET_ERR_INVALID_ARG
+    # a scale buffer of the 128 format handed to the 64 format is too small
+    with pytest.raises(ValueError, match="scales"):
+        bn.bitnet_w2a8_gemv_g(o["packed"], o["scales"], o["q"], o["s_a"], o["N"], o["K"], 64)
+
+
+def test_other_wrappers_check_their_outputs():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((3, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q"):
+        bn.bitnet_quant_act(x, q=torch.zeros((3, 128), dtype=torch.int8))
+    with pytest.raises(ValueError, match="s_a"):
+        bn.bitnet_quant_act(x, s_a=torch.zeros(2, dtype=torch.float32))
+    y2 = torch.zeros((3, 512), dtype=torch.float32)
+    with pytest.raises(ValueError, match="q"):
+        bn.bitnet_quant_act_fold(y2, q=torch.zeros((3, 512), dtype=torch.int8))
+    with pytest.raises(ValueError, match="s_a"):
+        bn.bitnet_quant_act_relu2_glu(y2, s_a=torch.zeros(4, dtype=torch.float32))
+    o = _operands(torch, M=1)
+    xb = torch.zeros((1, o["K"]), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q_out"):
+        bn.bitnet_w2a8_gemv_act(o["packed"], o["scales"], xb, o["N"], o["K"],
+                                q_out=torch.zeros((1, o["K"] // 2), dtype=torch.int8))
+    with pytest.raises(ValueError, match="y"):
+        bn.bitnet_w2a8_gemv_act(o["packed"], o["scales"], xb, o["N"], o["K"],
+                                y=torch.zeros((1, o["N"] + 16), dtype=torch.float32))
+    with pytest.raises(ValueError, match="acc"):
+        bn.bitnet_w2a8_gemv_lut(o["packed"], o["scales"], o["q"], o["s_a"], o["N"], o["K"],
+                                acc=torch.zeros((1, 16), dtype=torch.int32))
+    with pytest.raises(ValueError, match="sink"):
+        bn.bitnet_probe_stream_read(torch.zeros(4096, dtype=torch.uint8), sink=torch.zeros(0, dtype=torch.int32))
