@@ -81,6 +81,12 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--quick", action="store_true", help="headline only (no per-shape table)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-stack", action="store_true",
+                    help="for a kernel trace: the 30-layer stack's one-token graph (linear fold), replayed 5 times "
+                         "at batch 1 and 5 times at batch 8, synchronised after each replay")
+    ap.add_argument("--profile-shapes", action="store_true",
+                    help="short eager run for counter passes: a 64 MiB device copy (calibration), then 64 product "
+                         "launches each of 2560x2560, 2560x6912 and 20480x3200 at batch 1 and 13824x2560 at batch 8")
     ap.add_argument("--profile-run", action="store_true",
                     help="short eager run for hardware-counter passes: a 64 MiB device copy (the byte-count "
                          "calibration), 64 launches each of the headline product and fused step, 16 prefill products")
@@ -125,13 +131,26 @@ def capture(torch, launch, n):
     return g
 
 
-def time_graph(torch, g, reps):
-    """Replays g reps times between two events on the current stream; returns total ms."""
+def time_graph(torch, g, reps, pre=None, warm=True, idle_start=False):
+    """Replays g `reps` times between two events on the current stream; returns total ms.
+    First (untimed) one replay of g when `warm`, a synchronisation, then one replay of
+    `pre` (default: g itself) enqueued just before the first event: `pre` covers the whole
+    weight rotation, so every timed step finds its weights where the steady state of a
+    decode loop leaves them (its copy last read a full rotation, >= 512 MB, earlier, so
+    not in the 256 MB last-level cache), and the host submits the timed replays while
+    the GPU is still busy with `pre`, so the events bracket the steps' GPU work.  With
+    `idle_start` the GPU is synchronised after `pre` instead, so the host's submission of
+    the first timed replay falls inside the timed region: the difference between the two
+    is the graph launch overhead."""
     stream = torch.cuda.current_stream()
-    g.replay()
+    if warm:
+        g.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    (pre or g).replay()
+    if idle_start:
+        torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(reps):
         g.replay()
@@ -465,9 +484,12 @@ def cpu_baseline_all_cores(c, T, S, seconds, cores):
     }
 
 
-def cpu_baseline(wl, c, T, S, seconds):
+def cpu_baseline(wl, c, T, S, seconds, y_gpu=None):
     """The oracle, as it stands, timed single-threaded on this host on the
-    headline workload (quantise + product of the whole 13824x2560 matrix)."""
+    headline workload (quantise + product of the whole 13824x2560 matrix).  Its
+    result is also compared with the GPU's headline output: the worst error as a
+    fraction of the tolerance 1e-5 * max(|y|, mag) and the plain maximum relative
+    error."""
     import oracle
     P = oracle.pack_i2s(T)
     try:
@@ -484,6 +506,15 @@ def cpu_baseline(wl, c, T, S, seconds):
         if el >= seconds:
             break
     per = el / reps
+    parity = None
+    if y_gpu is not None:
+        ref = oracle.w2a8(P, S, q, s, c.N, c.K)
+        err = np.abs(y_gpu.astype(np.float64) - ref["y64"])
+        bound = 1e-5 * np.maximum(np.abs(ref["y64"]), ref["mag"])
+        nz = ref["y64"] != 0
+        parity = {"outputs": int(err.size), "worst_err_over_tolerance": float((err / bound).max()),
+                  "outside_tolerance": int(np.count_nonzero(err > bound)),
+                  "plain_max_rel_err": float((err[nz] / np.abs(ref["y64"][nz])).max())}
     model = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -497,6 +528,7 @@ def cpu_baseline(wl, c, T, S, seconds):
         "sample": f"{reps} full quantise+product passes of the 13824x2560 M=1 workload "
                   f"({per * 1e3:.1f} ms each, {el:.1f} s), single thread pinned to one core; CPU: {model}",
         "us_per_step": per * 1e6,
+        "parity_of_gpu_headline_output": parity,
     }
 
 
@@ -537,6 +569,67 @@ def profile_run(torch, bn, wl):
     log(f"profile run done: copy {n} B x3, gemv x64, fused x64, lut gemv x64, prefill 512x13824x2560 x16")
 
 
+def calibration_copy(torch):
+    """A plain 64 MiB device copy, three times: the known byte count the HBM counters are scaled by."""
+    n = 64 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def profile_stack(torch, bn, wl):
+    """One token of the 30-layer stack (180 products, linear fold) captured as a graph,
+    replayed 5 times at batch 1 and 5 times at batch 8, with a synchronisation after
+    every replay so each token stands alone in the trace."""
+    ws = []
+    for layer in range(wl.STACK_LAYERS):
+        for idx in range(6):
+            T, S = wl.stack_matrix(layer, idx)
+            ws.append(bn.PackedWeight.from_ternary(T, S))
+    for M in (1, 8):
+        chain = bn.Chain(ws, ["sum" if i % 6 == 5 else False for i in range(len(ws))])
+        x = torch.from_numpy(wl.stack_input(M).view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, wl.STACK_HIDDEN), dtype=torch.float32, device="cuda")
+        chain.workspace(M)
+        g = capture(torch, lambda i: chain(x, y=y), 1)
+        for _ in range(5):
+            g.replay()
+            torch.cuda.synchronize()
+        log(f"profile stack: batch {M}, 5 token replays done")
+        del g, chain
+
+
+def profile_shapes(torch, bn, wl):
+    """Counter passes over the decode shapes besides the headline: 64 product launches
+    each (weights rotated past the last-level cache) of 2560x2560, 2560x6912 and
+    20480x3200 at batch 1 and of 13824x2560 at batch 8."""
+    calibration_copy(torch)
+    cases = []
+    c1 = wl.config1()
+    cases.append(("gemv_2560x2560", c1.N, c1.K, 1, c1.T, c1.S, c1.x_bits))
+    T5, S5 = wl.stack_matrix(0, 5)
+    cases.append(("gemv_2560x6912", 2560, 6912, 1, T5, S5, wl.normal_act(wl.rng_for(5, 99), 1, 6912)))
+    c3 = wl.config3()
+    cases.append(("gemv_20480x3200", c3.N, c3.K, 1, c3.T, c3.S, c3.x_bits))
+    c2 = wl.config2(M=8)
+    T2, S2 = bn.bitnet_ternarize_absmean(c2.W)
+    cases.append(("gemv_13824x2560_m8", c2.N, c2.K, 8, T2, S2, c2.x_bits))
+    for name, N, K, M, T, S, xb in cases:
+        d = DecodeShape(torch, bn, name, N, K, M, T, S, xb)
+        d.quant(0)
+        torch.cuda.synchronize()
+        for i in range(64):
+            d.gemv(i)
+        torch.cuda.synchronize()
+        log(f"profile shapes: {name} batch {M}: 64 product launches done")
+        del d
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -554,6 +647,12 @@ def main():
     if args.profile_run:
         profile_run(torch, bn, wl)
         return
+    if args.profile_stack:
+        profile_stack(torch, bn, wl)
+        return
+    if args.profile_shapes:
+        profile_shapes(torch, bn, wl)
+        return
 
     # ---- headline workload: 13824x2560, M=1, absmean-ternarised N(0,0.02) weights
     c = wl.config2(M=1)
@@ -563,11 +662,19 @@ def main():
     for i in range(args.warmup):
         d.fused(i)
     torch.cuda.synchronize()
-    # exactly `steps` decode steps (one quantise-and-multiply launch each),
-    # captured once as a HIP graph and replayed
+    # exactly `steps` decode steps (one quantise-and-multiply launch each, step i on
+    # weight copy i mod R), captured once as a HIP graph.  Before the timed replay: one
+    # untimed replay of it, then one replay of a graph over the whole rotation (steps on
+    # copies 0..R-1), enqueued without waiting, so that the timed steps start in the
+    # steady state of the rotation and the host's submission overlaps GPU work
     g = capture(torch, d.fused, args.steps)
-    total_ms = time_graph(torch, g, 1)
+    g_rot = capture(torch, d.fused, d.rot.R)
+    total_ms = time_graph(torch, g, 1, pre=g_rot)
     ms_per_step = total_ms / args.steps
+    # the same replay started on an idle GPU: the host's submission is then inside the
+    # timed region; the difference is the graph launch overhead (not part of `value`)
+    idle_ms = time_graph(torch, g, 1, pre=g_rot, warm=False, idle_start=True)
+    graph_launch_overhead_us = (idle_ms - total_ms) * 1e3
     # the product kernel alone (pre-quantised input): one graph over the weight rotation
     reps = max(1, args.steps // d.rot.R)
     gemv_us = graph_us_per_launch(torch, d.gemv, d.rot.R, reps)
@@ -575,8 +682,9 @@ def main():
     step2_us = graph_us_per_launch(torch, d.step2, d.rot.R, reps)
     eager_us = eager_us_per_launch(torch, d.fused, min(args.steps, 500))
     # spread: ten more timed replays of the headline graph (not part of `value`)
-    rep_us = sorted(time_graph(torch, g, 1) * 1e3 / args.steps for _ in range(10))
-    del g
+    rep_us = sorted(time_graph(torch, g, 1, pre=g_rot, warm=False) * 1e3 / args.steps for _ in range(10))
+    del g, g_rot
+    y_headline = d.y.cpu().numpy().copy()
 
     N, K, M = c.N, c.K, c.M
     pbytes = N * K // 4
@@ -607,7 +715,15 @@ def main():
         "arithmetic": "int8 activations x ternary weights -> int32 per 128-weight block, fp32 epilogue",
         "data": "synthetic (seeded; absmean-ternarised N(0,0.02) weights, N(0,1) bf16 activations)",
         "config": {"workload": "gemv_13824x2560_m1", "M": M, "N": N, "K": K,
-                   "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32)},
+                   "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32),
+                   "timed_copies": min(args.steps, d.rot.R),
+                   "timed_weight_bytes": args.steps * (pbytes + N * K // 32),
+                   "timing": "one graph replay of exactly `steps` steps, step i on weight copy i mod "
+                             "rotation_copies; enqueued right behind an untimed replay of one full rotation "
+                             "(rotation_bytes >= 2 x the 256 MB last-level cache), so each timed step reads a "
+                             "copy last touched a full rotation earlier and the host's submission overlaps "
+                             "GPU work"},
+        "graph_launch_overhead_us": graph_launch_overhead_us,
         "step_us": ms_per_step * 1e3,
         "step_us_repeats": {"n": len(rep_us), "median": (rep_us[4] + rep_us[5]) / 2, "min": rep_us[0],
                             "max": rep_us[-1]},
@@ -631,6 +747,7 @@ def main():
             "product_kernel_at_scale": at_scale,
         },
     }
+    log(f"headline: graph launch overhead {graph_launch_overhead_us:.2f} us per replay (outside the timed steps)")
     log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
         f"gemv {gemv_us:.2f} us, quant {quant_us:.2f} us, two-launch step {step2_us:.2f} us, "
         f"eager step {eager_us:.2f} us; a bare read of the same {attain['bytes']} B takes {attain['us']:.2f} us "
@@ -676,7 +793,7 @@ def main():
     if not args.no_cpu:
         cores = sorted(os.sched_getaffinity(0))
         result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(c, T, S, min(args.cpu_seconds, 8.0), cores)
-        result["cpu_baseline"] = cpu_baseline(wl, c, T, S, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, c, T, S, args.cpu_seconds, y_headline)
     print(json.dumps(result), flush=True)
 
 

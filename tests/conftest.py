@@ -19,3 +19,27 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU test collected on a machine without a GPU")
     return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _parity_test_name(request):
+    import parity_stats
+    parity_stats.CURRENT = request.node.nodeid
+    yield
+
+
+def pytest_terminal_summary(terminalreporter):
+    try:
+        import parity_stats
+    except ImportError:
+        return
+    if not parity_stats.STATS:
+        return
+    tr = terminalreporter
+    tr.section("fp32 parity against the oracle: worst error / tolerance, plain max relative error")
+    worst_r = max(r for r, _ in parity_stats.STATS.values())
+    worst_p = max(p for _, p in parity_stats.STATS.values())
+    for name, (r, p) in sorted(parity_stats.STATS.items()):
+        tr.write_line(f"{r:9.3f}  {p:10.3e}  {name}")
+    tr.write_line(f"overall: worst error / tolerance {worst_r:.3f}; plain max relative error {worst_p:.3e} "
+                  f"over {len(parity_stats.STATS)} tests")

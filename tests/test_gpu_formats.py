@@ -11,6 +11,7 @@ import pytest
 
 import bit_gemv_i2_amd as bn
 import oracle
+import parity_stats
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +30,7 @@ def host(t):
 
 
 def close(y, ref, what):
+    parity_stats.record(y, ref["y64"], ref["mag"])
     bound = RTOL * np.maximum(np.abs(ref["y64"]), ref["mag"])
     err = np.abs(y.astype(np.float64) - ref["y64"])
     assert not (err > bound).any(), f"{what}: {(err > bound).sum()} outside, worst {(err / bound).max():.3g}x"

@@ -7,6 +7,7 @@ import pytest
 
 import bit_gemv_i2_amd as bn
 import oracle
+import parity_stats
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +31,7 @@ def check(T, S, q, s_a, tiles, what):
     p, st = bn.bitnet_pack_i2s(T, S)
     y, acc = bn.bitnet_w2a8_gemv_lut(dev(p), dev(st), dev(q), dev(s_a), N, K, tiles, with_acc=True)
     assert np.array_equal(host(acc), ref["acc"]), f"{what}: int32 sums differ"
+    parity_stats.record(host(y), ref["y64"], ref["mag"])
     bound = RTOL * np.maximum(np.abs(ref["y64"]), ref["mag"])
     err = np.abs(host(y).astype(np.float64) - ref["y64"])
     assert not (err > bound).any(), f"{what}: {(err > bound).sum()} outputs outside tolerance"

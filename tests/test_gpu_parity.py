@@ -11,6 +11,7 @@ import pytest
 
 import bit_gemv_i2_amd as bn
 import oracle
+import parity_stats
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -39,6 +40,7 @@ def pack_dev(T, S):
 
 def assert_f32_close(y, ref, what=""):
     y64, mag = ref["y64"], ref["mag"]
+    parity_stats.record(y, y64, mag)
     bound = RTOL * np.maximum(np.abs(y64), mag)
     err = np.abs(y.astype(np.float64) - y64)
     bad = err > bound
@@ -351,23 +353,34 @@ def test_stack_shapes_gemv_full(gpu, idx, M):
 
 
 @pytest.mark.slow
-def test_config4_gemm_full_sampled(gpu):
+def test_config4_gemm_full(gpu):
+    """The whole 512 x 13824 output of the prefill workload (int32 sums, bf16 and fp32
+    results) against the oracle, which runs its rows in a process pool."""
+    import oracle_pool as op
     c = wl.config4()
     qd, sd = bn.bitnet_quant_act(x_dev(c.x_bits))
     qo, so = oracle.quant_act_bf16(c.x_bits)
     assert np.array_equal(host(qd), qo) and np.array_equal(host(sd), so)
     p, st = pack_dev(c.T, c.S)
-    y = bn.bitnet_w2a8_gemm(p, st, qd, sd, c.N, c.K)
-    ybits = host(y.view(torch.int16)).view(np.uint16)
+    ybits = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, c.N, c.K).view(torch.int16)).view(np.uint16)
+    y32 = host(bn.bitnet_w2a8_gemm(p, st, qd, sd, c.N, c.K, out_dtype=torch.float32))
     acc = host(bn.bitnet_w2a8_acc_i32(p, qd, c.N, c.K))
-    r = wl.rng_for(54)
-    toks = np.sort(r.choice(c.M, 48, replace=False))
-    toks[0], toks[-1] = 0, c.M - 1
-    rows = np.sort(r.choice(c.N, 640, replace=False))
-    rows[0], rows[-1] = 0, c.N - 1
-    ref = oracle.w2a8(oracle.pack_i2s(c.T[rows]), c.S[rows], qo[toks], so[toks], len(rows), c.K)
-    assert np.array_equal(acc[np.ix_(toks, rows)], ref["acc"])
-    assert_bf16_ok(ybits[np.ix_(toks, rows)], ref, "config4 sampled")
+    step = 432
+    print(f"config4: oracle on {c.M} x {c.N} outputs in {op.workers()} processes", flush=True)
+    seen = 0
+    worst = plain = 0.0
+    with op.pool() as ex:
+        for n0, acc_o, y64, mag in ex.map(op.config4_rows, range(0, c.N, step), range(step, c.N + step, step)):
+            n1 = n0 + acc_o.shape[1]
+            ref = {"y64": y64, "mag": mag}
+            assert np.array_equal(acc[:, n0:n1], acc_o), f"int32 sums differ in rows {n0}..{n1}"
+            assert_bf16_ok(ybits[:, n0:n1], ref, f"config4 bf16 rows {n0}..{n1}")
+            assert_f32_close(y32[:, n0:n1], ref, f"config4 f32 rows {n0}..{n1}")
+            r, _, pl = op.f32_check(y32[:, n0:n1], y64, mag)
+            worst, plain = max(worst, r), max(plain, pl)
+            seen += n1 - n0
+    assert seen == c.N
+    print(f"config4: every output checked; fp32 worst error / bound {worst:.3f}, plain max relative error {plain:.3e}")
 
 
 # ------------------------------------------------------------------ prefill row-tile choices

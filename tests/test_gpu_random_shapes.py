@@ -14,6 +14,7 @@ import pytest
 
 import bit_gemv_i2_amd as bn
 import oracle
+import parity_stats
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +47,7 @@ def draw_shapes(seed, n, m_lo, m_hi):
 
 
 def f32_ok(y, ref):
+    parity_stats.record(y, ref["y64"], ref["mag"])
     bound = RTOL * np.maximum(np.abs(ref["y64"]), ref["mag"])
     return np.abs(y.astype(np.float64) - ref["y64"]) <= bound
 
