@@ -88,6 +88,9 @@ _SIGS = {
     "bitnet_w2a8_chain_workspace_bytes": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
     "bitnet_w2a8_chain": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_chain_static_max_bytes": ([], ctypes.c_size_t),
+    "bitnet_w2a8_chain_static": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
 
 
@@ -585,6 +588,29 @@ class Chain:
                                     M, _dev_ptr(y, "y"), _dev_ptr(ws, "workspace"), ws.numel(), _stream(stream)),
             "bitnet_w2a8_chain")
         return y
+
+
+    def call_static(self, x, y=None, stream=None):
+        """The same pass through bitnet_w2a8_chain_static: no workspace is allocated (the
+        library's per-GPU array serves), for callers that cannot allocate."""
+        import torch
+        M = x.shape[0]
+        xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
+        if xdt is None:
+            raise ValueError("x must be bf16 or fp32")
+        if x.dim() != 2 or x.shape[1] != self.weights[0].K:
+            raise ValueError(f"x must be [M][{self.weights[0].K}], not {tuple(x.shape)}")
+        if y is None:
+            y = torch.empty((M, self.weights[-1].N), dtype=torch.float32, device=x.device)
+        _check(y, "y", torch.float32, numel=M * self.weights[-1].N)
+        _ok(lib().bitnet_w2a8_chain_static(ctypes.cast(self._arr, ctypes.c_void_p), len(self.weights),
+                                           _dev_ptr(x, "x"), xdt, M, _dev_ptr(y, "y"), _stream(stream)),
+            "bitnet_w2a8_chain_static")
+        return y
+
+
+def bitnet_w2a8_chain_static_max_bytes() -> int:
+    return lib().bitnet_w2a8_chain_static_max_bytes()
 
 
 # ------------------------------------------------------------------ measurement helper

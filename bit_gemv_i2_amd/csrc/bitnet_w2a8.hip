@@ -1719,17 +1719,12 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
     return chain_plan(layers, n, M, layers[0].K, &plan) == BITNET_OK ? plan.total : 0;
 }
 
-bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
-                                  float *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!x || !y || !workspace || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
-        return BITNET_ERR_INVALID_ARG;
-    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
-    if (!layers || n < 1) return BITNET_ERR_INVALID_ARG;
-    ChainPlan plan;
-    const bitnet_status_t st = chain_plan(layers, n, M, layers[0].K, &plan);
-    if (st != BITNET_OK) return st;
-    if (workspace_bytes < plan.total) return BITNET_ERR_INVALID_ARG;
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
+}  // extern "C"
+
+namespace {
+// The chain's launches, with the workspace already checked against the plan.
+bitnet_status_t chain_run(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M, float *y,
+                          unsigned char *ws, const ChainPlan &plan, hipStream_t stream) {
     float *act[2] = {reinterpret_cast<float *>(ws), reinterpret_cast<float *>(ws + plan.act_bytes)};
     int8_t *q = reinterpret_cast<int8_t *>(ws + 2 * plan.act_bytes);
     float *s_a = reinterpret_cast<float *>(ws + 2 * plan.act_bytes + plan.q_bytes);
@@ -1779,6 +1774,69 @@ bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, con
         in_dt = BITNET_DT_F32;
     }
     return BITNET_OK;
+}
+
+// Argument checks shared by both chain entry points; fills the plan.
+bitnet_status_t chain_check(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M, const float *y,
+                            ChainPlan *plan) {
+    if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return BITNET_ERR_INVALID_ARG;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
+    if (!layers || n < 1) return BITNET_ERR_INVALID_ARG;
+    return chain_plan(layers, n, M, layers[0].K, plan);
+}
+
+// Workspace of bitnet_w2a8_chain_static: one array per GPU, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is only a stand-in
+// for the device symbol); it uses the device address hipGetSymbolAddress reports, looked
+// up once per device with that device current and kept per device.
+constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::atomic<uintptr_t> g_scratch_ptr[kSlotCacheDevices];
+
+bitnet_status_t static_scratch(hipStream_t stream, unsigned char **out) {
+    int dev = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return BITNET_ERR_HIP;
+    if (dev < 0 || dev >= kSlotCacheDevices) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return BITNET_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return BITNET_ERR_HIP;
+        void *addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return BITNET_ERR_HIP;
+        if (e != hipSuccess || addr == nullptr) return BITNET_ERR_HIP;
+        p = reinterpret_cast<uintptr_t>(addr);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);  // the same value on every thread
+    }
+    *out = reinterpret_cast<unsigned char *>(p);
+    return BITNET_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
+                                  float *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    ChainPlan plan;
+    const bitnet_status_t st = chain_check(layers, n, x, xdt, M, y, &plan);
+    if (st != BITNET_OK) return st;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < plan.total) return BITNET_ERR_INVALID_ARG;
+    return chain_run(layers, n, x, xdt, M, y, static_cast<unsigned char *>(workspace), plan, stream);
+}
+
+size_t bitnet_w2a8_chain_static_max_bytes(void) { return kStaticScratchBytes; }
+
+bitnet_status_t bitnet_w2a8_chain_static(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
+                                         float *y, hipStream_t stream) {
+    ChainPlan plan;
+    bitnet_status_t st = chain_check(layers, n, x, xdt, M, y, &plan);
+    if (st != BITNET_OK) return st;
+    if (plan.total > kStaticScratchBytes) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    unsigned char *ws = nullptr;
+    st = static_scratch(stream, &ws);
+    if (st != BITNET_OK) return st;
+    return chain_run(layers, n, x, xdt, M, y, ws, plan, stream);
 }
 
 }  // extern "C"

@@ -29,7 +29,9 @@
  *     No C++ exception crosses this interface.
  *   - Ownership: the caller owns every buffer.  The library allocates no
  *     memory and is re-entrant; the only state it keeps between calls is a
- *     cache of each device's CU count and wave slots, read on first use.
+ *     cache of each device's CU count and wave slots, read on first use, and
+ *     the fixed per-GPU workspace array of bitnet_w2a8_chain_static (whose
+ *     device address is looked up on first use).
  *   - "device" pointers are HIP device memory, 16-byte aligned; "host"
  *     pointers are ordinary host memory.  Non-finite inputs are outside the
  *     contract.
@@ -310,6 +312,23 @@ size_t bitnet_w2a8_chain_workspace_bytes(const bitnet_chain_layer_t *layers, int
  * Enqueues everything on `stream` (capturable in a HIP graph); no allocation. */
 bitnet_status_t bitnet_w2a8_chain(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
                                   float *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* bitnet_w2a8_chain for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation: the same launches
+ * and results as bitnet_w2a8_chain, with the workspace in a fixed array the library holds
+ * on each GPU (bitnet_w2a8_chain_static_max_bytes() = 4 MiB, kept until the process ends)
+ * instead of a caller buffer.  Calls no allocating routine.  The first call on a device
+ * looks up the array's device address (with that device made current for the lookup and
+ * the caller's current device restored).  Every call on one GPU uses the same array, so
+ * calls that overlap in time on one GPU (different streams, or host threads) race and
+ * give undefined results; calls ordered on one stream are safe.  Nothing in the array
+ * needs to start at zero: every intermediate value is written before it is read.
+ *   layers, n, x, xdt, M, y   as bitnet_w2a8_chain
+ * Rules: as bitnet_w2a8_chain, and bitnet_w2a8_chain_workspace_bytes(layers, n, M) at most
+ * bitnet_w2a8_chain_static_max_bytes() (else BITNET_ERR_UNSUPPORTED_SHAPE, no launch). */
+size_t bitnet_w2a8_chain_static_max_bytes(void);
+bitnet_status_t bitnet_w2a8_chain_static(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
+                                         float *y, hipStream_t stream);
 
 /* Exact integer product acc[m][n] = sum_k T[n][k] * Q[m][k] (int32, device, [M][N]),
  * computed by the same kernels as the two products above (M <= 16: the decode
