@@ -12,8 +12,9 @@ than twice the 256 MB last-level cache, so the weight stream comes from HBM.
 value = packed-weight bytes (N*K/4) per step / step time, in GB/s.
 The roofline object prices the step's kernel against 8 TB/s using its
 algorithmic bytes (packed weights + fp32 block scales + bf16 activations +
-fp32 outputs) over its average duration in the timed region (HIP events on the
-launch stream around the captured steps, one launch each); "product_kernel"
+fp32 outputs) over its average duration in the timed region (one launch per step;
+the steps are timed by HIP events on the launch stream, as the difference of two graph
+replays so that the fixed cost of a replay cancels, see config.timing); "product_kernel"
 gives the same for the product alone (int8 q in).  Beside them,
 "attainable_read" is what one bare pass of 16-byte non-temporal loads (the
 hint the product's weight loads carry) over the same number of bytes achieves
@@ -131,17 +132,14 @@ def capture(torch, launch, n):
     return g
 
 
-def time_graph(torch, g, reps, pre=None, warm=True, idle_start=False):
+def time_graph(torch, g, reps, pre=None, warm=True):
     """Replays g `reps` times between two events on the current stream; returns total ms.
     First (untimed) one replay of g when `warm`, a synchronisation, then one replay of
     `pre` (default: g itself) enqueued just before the first event: `pre` covers the whole
     weight rotation, so every timed step finds its weights where the steady state of a
     decode loop leaves them (its copy last read a full rotation, >= 512 MB, earlier, so
     not in the 256 MB last-level cache), and the host submits the timed replays while
-    the GPU is still busy with `pre`, so the events bracket the steps' GPU work.  With
-    `idle_start` the GPU is synchronised after `pre` instead, so the host's submission of
-    the first timed replay falls inside the timed region: the difference between the two
-    is the graph launch overhead."""
+    the GPU is still busy with `pre`, so the events bracket the steps' GPU work."""
     stream = torch.cuda.current_stream()
     if warm:
         g.replay()
@@ -149,14 +147,34 @@ def time_graph(torch, g, reps, pre=None, warm=True, idle_start=False):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     (pre or g).replay()
-    if idle_start:
-        torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(reps):
         g.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1)
+
+
+def steps_by_difference(torch, launch, n, R, reps=10):
+    """Times exactly n steady-state steps: graph A runs steps on copies 0..R-1 (one whole
+    rotation), graph B the same R steps and then n more on copies 0, 1, ... (so each of the
+    n extra steps reads a copy last touched a full rotation earlier, as in a decode loop).
+    Each replay is timed by events on the launch stream, behind an untimed full rotation
+    that hides the host's submission.  T(B) - T(A) holds exactly the n extra steps' GPU
+    work: the fixed cost of a graph replay (the same in both) cancels.  Returns the
+    per-repeat differences in ms (A and B alternate, `reps` times)."""
+    gA = capture(torch, launch, R)
+    gB = capture(torch, lambda i: launch(i if i < R else i - R), R + n)
+    gA.replay()
+    gB.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        a = time_graph(torch, gA, 1, pre=gA, warm=False)
+        b = time_graph(torch, gB, 1, pre=gA, warm=False)
+        out.append(b - a)
+    del gA, gB
+    return out
 
 
 def graph_us_per_launch(torch, launch, n, reps):
@@ -663,18 +681,17 @@ def main():
         d.fused(i)
     torch.cuda.synchronize()
     # exactly `steps` decode steps (one quantise-and-multiply launch each, step i on
-    # weight copy i mod R), captured once as a HIP graph.  Before the timed replay: one
-    # untimed replay of it, then one replay of a graph over the whole rotation (steps on
-    # copies 0..R-1), enqueued without waiting, so that the timed steps start in the
-    # steady state of the rotation and the host's submission overlaps GPU work
+    # weight copy i mod R); for reference also timed as one replay of a graph of just them
     g = capture(torch, d.fused, args.steps)
     g_rot = capture(torch, d.fused, d.rot.R)
-    total_ms = time_graph(torch, g, 1, pre=g_rot)
+    whole_replay_ms = time_graph(torch, g, 1, pre=g_rot)
+    # `steps` steady-state steps, as the difference of two event-timed graph replays (one
+    # rotation, and the same rotation followed by the `steps` steps): the median of ten
+    diffs = sorted(steps_by_difference(torch, d.fused, args.steps, d.rot.R))
+    total_ms = (diffs[4] + diffs[5]) / 2
     ms_per_step = total_ms / args.steps
-    # the same replay started on an idle GPU: the host's submission is then inside the
-    # timed region; the difference is the graph launch overhead (not part of `value`)
-    idle_ms = time_graph(torch, g, 1, pre=g_rot, warm=False, idle_start=True)
-    graph_launch_overhead_us = (idle_ms - total_ms) * 1e3
+    # what one replay of a graph of just the `steps` steps costs beyond them (not in `value`)
+    graph_replay_fixed_us = (whole_replay_ms - total_ms) * 1e3
     # the product kernel alone (pre-quantised input): one graph over the weight rotation
     reps = max(1, args.steps // d.rot.R)
     gemv_us = graph_us_per_launch(torch, d.gemv, d.rot.R, reps)
@@ -682,7 +699,7 @@ def main():
     step2_us = graph_us_per_launch(torch, d.step2, d.rot.R, reps)
     eager_us = eager_us_per_launch(torch, d.fused, min(args.steps, 500))
     # spread: ten more timed replays of the headline graph (not part of `value`)
-    rep_us = sorted(time_graph(torch, g, 1, pre=g_rot, warm=False) * 1e3 / args.steps for _ in range(10))
+    rep_us = [x * 1e3 / args.steps for x in diffs]
     del g, g_rot
     y_headline = d.y.cpu().numpy().copy()
 
@@ -718,12 +735,16 @@ def main():
                    "rotation_copies": d.rot.R, "rotation_bytes": d.rot.R * (pbytes + N * K // 32),
                    "timed_copies": min(args.steps, d.rot.R),
                    "timed_weight_bytes": args.steps * (pbytes + N * K // 32),
-                   "timing": "one graph replay of exactly `steps` steps, step i on weight copy i mod "
-                             "rotation_copies; enqueued right behind an untimed replay of one full rotation "
-                             "(rotation_bytes >= 2 x the 256 MB last-level cache), so each timed step reads a "
-                             "copy last touched a full rotation earlier and the host's submission overlaps "
-                             "GPU work"},
-        "graph_launch_overhead_us": graph_launch_overhead_us,
+                   "timing": "exactly `steps` steps, step i on weight copy i mod rotation_copies, in the "
+                             "steady state of the rotation (rotation_bytes >= 2 x the 256 MB last-level cache: "
+                             "each step reads a copy last touched a full rotation earlier); timed as the "
+                             "difference of two event-timed replays of HIP graphs, one over a whole rotation "
+                             "and one over the same rotation followed by the `steps` steps, so the fixed cost "
+                             "of a graph replay cancels (median of 10 pairs); step_us_whole_replay times one "
+                             "replay of a graph of just the `steps` steps instead, that fixed cost "
+                             "(graph_replay_fixed_us) included"},
+        "graph_replay_fixed_us": graph_replay_fixed_us,
+        "step_us_whole_replay": whole_replay_ms * 1e3 / args.steps,
         "step_us": ms_per_step * 1e3,
         "step_us_repeats": {"n": len(rep_us), "median": (rep_us[4] + rep_us[5]) / 2, "min": rep_us[0],
                             "max": rep_us[-1]},
@@ -747,7 +768,9 @@ def main():
             "product_kernel_at_scale": at_scale,
         },
     }
-    log(f"headline: graph launch overhead {graph_launch_overhead_us:.2f} us per replay (outside the timed steps)")
+    log(f"headline: a replay of a graph of just the {args.steps} steps takes {whole_replay_ms * 1e3:.1f} us "
+        f"({whole_replay_ms * 1e3 / args.steps:.2f} us a step): {graph_replay_fixed_us:.1f} us of fixed cost per "
+        f"graph replay on the GPU (not in the timed steps)")
     log(f"headline: {ms_per_step * 1e3:.2f} us/step ({result['value']:.0f} GB/s packed), "
         f"gemv {gemv_us:.2f} us, quant {quant_us:.2f} us, two-launch step {step2_us:.2f} us, "
         f"eager step {eager_us:.2f} us; a bare read of the same {attain['bytes']} B takes {attain['us']:.2f} us "
