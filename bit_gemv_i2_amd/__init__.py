@@ -89,6 +89,14 @@ _SIGS = {
     "bitnet_w2a8_chain": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_chain_static_max_bytes": ([], ctypes.c_size_t),
+    "bitnet_w2a8_persist_table_bytes": ([ctypes.c_int], ctypes.c_size_t),
+    "bitnet_w2a8_persist_prepare": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "bitnet_w2a8_chain_persistent": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "bitnet_w2a8_chain_persistent_ex": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p], ctypes.c_int),
     "bitnet_w2a8_chain_static": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
@@ -590,6 +598,57 @@ class Chain:
         return y
 
 
+    def plan_persistent(self, M: int = 1, xdt: int = BITNET_DT_BF16, cus: int = 0, device="cuda"):
+        key = ("persistent", M, xdt, cus)
+        if key not in self._ws:
+            self._ws[key] = PersistentPlan(self, M, xdt, cus, device)
+        return self._ws[key]
+
+    def persistent(self, x, y=None, stream=None, workspace=None, spin_limit: int = 0, withhold: int = -1):
+        """The same decode pass as one persistent launch (bitnet_w2a8_chain_persistent, batch 1).
+        Returns y; the workspace (which the binding allocates unless one is given) then
+        holds the status word (int32 at offset 0: 0; the layer index + 1 of a wait that
+        gave up; minus (layer index + 1) of a table entry that does not fit the workspace)
+        and every intermediate layer's output.  spin_limit / withhold are the
+        test-only knobs of bitnet_w2a8_chain_persistent_ex."""
+        import torch
+        M = x.shape[0]
+        xdt = {torch.bfloat16: BITNET_DT_BF16, torch.float32: BITNET_DT_F32}.get(x.dtype)
+        if xdt is None:
+            raise ValueError("x must be bf16 or fp32")
+        if x.dim() != 2 or x.shape[1] != self.weights[0].K:
+            raise ValueError(f"x must be [M][{self.weights[0].K}], not {tuple(x.shape)}")
+        plan = self.plan_persistent(M, xdt, device=x.device)
+        if y is None:
+            y = torch.empty((M, self.weights[-1].N), dtype=torch.float32, device=x.device)
+        _check(y, "y", torch.float32, numel=M * self.weights[-1].N)
+        if workspace is None:
+            wkey = ("persistent_ws", M, xdt)
+            if wkey not in self._ws:
+                self._ws[wkey] = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=x.device)
+            workspace = self._ws[wkey]
+        _check(workspace, "workspace", torch.uint8)
+        if workspace.numel() < plan.workspace_bytes:
+            raise ValueError(f"workspace must hold at least {plan.workspace_bytes} bytes")
+        _ok(lib().bitnet_w2a8_chain_persistent_ex(_dev_ptr(plan.table, "table"), plan.n, _dev_ptr(x, "x"), xdt, M,
+                                                  _dev_ptr(y, "y"), _dev_ptr(workspace, "workspace"),
+                                                  workspace.numel(), int(spin_limit), int(withhold), _stream(stream)),
+            "bitnet_w2a8_chain_persistent")
+        return y
+
+    def persistent_layer_outputs(self, M: int = 1, xdt: int = BITNET_DT_BF16):
+        """Host views (fp32 [M][N]) of every intermediate layer's output as the last
+        persistent call left them in the binding's workspace, and the status word."""
+        plan = self.plan_persistent(M, xdt)
+        ws = self._ws[("persistent_ws", M, xdt)].cpu().numpy()
+        table = plan.host_table.view(np.int64).reshape(plan.n, 8)  # out_off is the 4th 8-byte field
+        outs = []
+        for i in range(plan.n - 1):
+            off = int(table[i, 3])
+            N = self.weights[i].N
+            outs.append(ws[off:off + 4 * M * N].view(np.float32).reshape(M, N).copy())
+        return outs, int(ws[:4].view(np.int32)[0])
+
     def call_static(self, x, y=None, stream=None):
         """The same pass through bitnet_w2a8_chain_static: no workspace is allocated (the
         library's per-GPU array serves), for callers that cannot allocate."""
@@ -607,6 +666,25 @@ class Chain:
                                            _dev_ptr(x, "x"), xdt, M, _dev_ptr(y, "y"), _stream(stream)),
             "bitnet_w2a8_chain_static")
         return y
+
+
+class PersistentPlan:
+    """The layer table and workspace size of the one-launch (persistent) form of a chain,
+    from bitnet_w2a8_persist_prepare (host), with the table copied to the device once:
+    the weights' addresses are fixed, so a plan serves every later call."""
+
+    def __init__(self, chain: "Chain", M: int, xdt: int, cus: int = 0, device="cuda"):
+        import torch
+        n = len(chain.weights)
+        nb = lib().bitnet_w2a8_persist_table_bytes(n)
+        host = np.zeros(nb, np.uint8)
+        ws = ctypes.c_size_t(0)
+        _ok(lib().bitnet_w2a8_persist_prepare(ctypes.cast(chain._arr, ctypes.c_void_p), n, M, xdt, cus,
+                                              _np_ptr(host), nb, ctypes.byref(ws)), "bitnet_w2a8_persist_prepare")
+        self.host_table = host
+        self.table = torch.from_numpy(host).to(device)
+        self.workspace_bytes = ws.value
+        self.n = n
 
 
 def bitnet_w2a8_chain_static_max_bytes() -> int:

@@ -1840,3 +1840,514 @@ bitnet_status_t bitnet_w2a8_chain_static(const bitnet_chain_layer_t *layers, int
 }
 
 }  // extern "C"
+
+// --------------------------------------------------------------------------
+// a7, persistent form: the whole decode chain in one launch, batch 1.
+//
+// The chained products ([P2] "Architecture foundations": W2A8 GEMV; [P3] "Why WASM":
+// a ternary model's layers) depend on each other only through each layer's full output
+// vector, and at batch 1 a layer is a few microseconds of dependent latency against
+// well under a microsecond of weight stream.  Here one 16-wave workgroup per CU runs
+// every layer in turn; a layer's row tiles are spread over the first `nwg` workgroups
+// (1, 2 or 4 tiles each), and:
+//  - each layer writes its fp32 output into a buffer of its own that was filled with a
+//    NaN pattern (0xFFFFFFFF, never a result of finite inputs) before the launch, with
+//    agent-scope stores; the next layer's workgroups read the whole vector with
+//    agent-scope loads and read again what still holds the pattern, until nothing does.
+//    No fence and no shared counter: a value that is no longer the pattern is final;
+//  - every workgroup requests a layer's weights (and block scales) into registers together
+//    with the layer's input, so that weights and input arrive in one wait;
+//  - every wait is bounded: after `spin_limit` rounds the workgroup writes the layer
+//    index + 1 into the status word and leaves, so the kernel always ends;
+//  - per tile the arithmetic is that of gemv_kernel's all-waves form: the input is
+//    quantised per token exactly as quant_act_kernel does (exact max, correctly rounded
+//    127 / amax, one fp32 multiply, half to even), waves split the blocks, each wave
+//    sums its blocks' scaled int32 tiles in order and the wave partials are added in
+//    wave order.  The split (waves per tile, blocks per wave) is this form's own, so the
+//    fp32 order -- and with it the last bits of y -- can differ from the
+//    launch-per-layer chain; both are within the product tolerance of the exact value.
+// --------------------------------------------------------------------------
+namespace {
+struct PLayer {
+    const uint8_t *packed;
+    const float *scales;
+    int64_t in_off;   // byte offset of the input in the workspace; -1: the caller's x
+    int64_t out_off;  // byte offset of the output in the workspace; -1: the caller's y
+    int N, K;
+    int xm;           // input: 0 bf16 / 1 fp32 caller x (ready), 4 fp32 layer output,
+                      // 5 two-half output folded, 6 two-half output gated
+    int tp;           // row tiles per workgroup
+    int nw, per;      // waves per tile, blocks per wave
+    int nwg;          // workgroups taking part
+    int pad;
+};
+static_assert(sizeof(PLayer) == 64, "PLayer is 64 bytes");
+
+// The layer table is read-only for the whole launch: read through the constant address
+// space, its fields arrive by scalar loads, which do not count against the vector-memory
+// counter that orders the input and weight requests.
+typedef __attribute__((address_space(4))) const PLayer CPLayer;
+
+struct PArgs {
+    const PLayer *table;
+    int n;
+    const void *x;
+    float *y;
+    unsigned char *ws;
+    int64_t ws_bytes;  // the caller's workspace size: every layer buffer must lie inside it
+    int *status;
+    int spin_limit;
+    int withhold;     // test only: the layer whose output is never stored (-1: none)
+};
+
+constexpr int kPWaves = 16;
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kPMaxK = 16384;        // 16 waves x 8 blocks x 128
+constexpr int kPMaxNB = 8;
+constexpr uint32_t kPending = 0xFFFFFFFFu;
+constexpr int kPCheapPolls = 64;     // single-line polls per round of waiting
+
+// Entry i of the layer table, read field by field through the constant address space.
+__device__ __forceinline__ PLayer p_entry(const PLayer *table, int i) {
+    CPLayer *t = (CPLayer *)table + i;
+    PLayer r;
+    r.packed = t->packed;
+    r.scales = t->scales;
+    r.in_off = t->in_off;
+    r.out_off = t->out_off;
+    r.N = t->N;
+    r.K = t->K;
+    r.xm = t->xm;
+    r.tp = t->tp;
+    r.nw = t->nw;
+    r.per = t->per;
+    r.nwg = t->nwg;
+    r.pad = 0;
+    return r;
+}
+
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The weights one wave needs for one layer: up to 8 blocks of its tile, two words and one
+// scale each.
+struct PWeights {
+    v2u w[kPMaxNB];
+    float s[kPMaxNB];
+};
+
+__device__ __forceinline__ void p_role(const PLayer &L, int wg, int w, bool *active, int *tile, int *b0, int *nb) {
+    const int ti = w / L.nw, wv = w - ti * L.nw;
+    const int nblk = L.K >> 7;
+    *tile = wg * L.tp + ti;
+    *b0 = wv * L.per;
+    *nb = min(L.per, nblk - *b0);
+    *active = wg < L.nwg && ti < L.tp && *tile < (L.N >> 4) && *nb > 0;
+}
+
+// Buffer loads: the base address and range sit in a scalar resource, each load takes a
+// 32-bit per-lane offset and a wave-uniform one, so a batch of loads costs one vector
+// register of addressing; a load past the range returns 0 instead of touching memory.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit dwords, gfx9-family resource format
+constexpr int kCpolSc1 = 16;            // cache policy: coherent at device (agent) scope
+constexpr int kCpolNt = 2;              // cache policy: non-temporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t p_rsrc(const void *base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)min(bytes, (size_t)0x7FFFFFF0u),
+                                             kRsrcWord3);
+}
+
+// Where one wave's weights for one layer start (wave-uniform), computed before any
+// request of the layer goes out.
+struct PWAddr {
+    __amdgpu_buffer_rsrc_t wr, sr;  // the layer's packed weights and block scales
+    uint32_t wo, so;                // byte offsets of the wave's first brick / first scale block
+    int nb;                         // blocks the wave sums (0 if idle)
+};
+
+__device__ __forceinline__ PWAddr p_weight_addr(const PLayer &L, int wg, int w) {
+    bool active;
+    int tile, b0, nb;
+    p_role(L, wg, w, &active, &tile, &b0, &nb);
+    const uint32_t base = active ? (uint32_t)(tile * (L.K >> 7) + b0) : 0u;
+    PWAddr r;
+    const size_t bricks = (size_t)(L.N >> 4) * (L.K >> 7);
+    r.wr = p_rsrc(L.packed, bricks * kBrickBytes);
+    r.sr = p_rsrc(L.scales, bricks * kTileN * sizeof(float));
+    r.wo = base * (uint32_t)kBrickBytes;
+    r.so = base * (uint32_t)(kTileN * sizeof(float));
+    r.nb = active ? nb : 0;
+    return r;
+}
+
+// Always 8 weight and 8 scale loads per lane (a fixed count, so that waiting for data
+// requested before them never waits for them): blocks past the wave's last read its last
+// one again (an idle wave reads the layer's first brick), which the caches hold.
+__device__ __forceinline__ void p_load_weights(const PWAddr &ad, int l, PWeights &r) {
+    const int last = ad.nb > 0 ? ad.nb - 1 : 0;
+    const uint32_t lw = (uint32_t)l * 8u, ls = (uint32_t)(l & 15) * 4u;
+#pragma unroll
+    for (int i = 0; i < kPMaxNB; ++i) {
+        const uint32_t bi = (uint32_t)(i < last ? i : last);
+        r.w[i] = __builtin_amdgcn_raw_buffer_load_b64(ad.wr, lw, ad.wo + bi * (uint32_t)kBrickBytes, kCpolNt);
+        r.s[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ad.sr, ls, ad.so + bi * (uint32_t)(kTileN * sizeof(float)), kCpolNt));
+    }
+}
+
+// One layer of the persistent chain.  Its weights are requested together with its input
+// (a request for the next layer's weights made before waiting here would delay every
+// read of the input: a wave's vector-memory requests complete in the order issued).
+__device__ __forceinline__ bool p_layer(const PArgs &a, int li, int8_t *qs, float *red, uint32_t *vote,
+                                        float *amax_part) {
+    const PLayer L = p_entry(a.table, li);
+    const int wg = blockIdx.x, t = threadIdx.x, l = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    // a table that does not fit the workspace it came with: every workgroup reads the same
+    // entry, so all of them stop here (status -(layer + 1)) and none waits on another
+    {
+        const int64_t in_end = L.in_off + (int64_t)(L.xm >= 5 ? 2 * L.K : L.K) * 4;
+        const int64_t out_end = L.out_off + (int64_t)L.N * 4;
+        const bool shape_ok = L.K >= (int)kBlockK && (L.K & (kBlockK - 1)) == 0 && L.N >= (int)kTileN &&
+                              (L.N & (kTileN - 1)) == 0 && L.K <= (L.xm >= 5 ? kPMaxK / 2 : kPMaxK) &&
+                              (L.tp == 1 || L.tp == 2 || L.tp == 4) && L.nw * L.tp == kPWaves && L.per >= 1 &&
+                              L.per <= kPMaxNB && L.per * L.nw * (int)kBlockK >= L.K;
+        if (!shape_ok || (L.xm >= 4 && (L.in_off < 256 || in_end > a.ws_bytes)) ||
+            (L.out_off >= 0 && (L.out_off < 256 || out_end > a.ws_bytes))) {
+            if (blockIdx.x == 0 && threadIdx.x == 0)
+                __hip_atomic_store(a.status, -(li + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+    }
+    const bool part = wg < L.nwg;
+    const int K = L.K;
+    const int xm = L.xm;
+
+    // (1) this thread's input: elements t, t + 1024, ... (16 of a plain input, or 8 of each
+    //     half of a two-half input), so that every load instruction of a wave reads 256
+    //     consecutive bytes.  Requested with agent-scope loads (always 16 of them; those
+    //     past the input read 0 without a memory request), then the layer's weights; the words are checked only after
+    //     both requests are out, so that check waits for the input alone.
+    constexpr int NE = kPMaxK / kPThreads;  // 16 elements per thread at most
+    uint32_t u[NE];  // raw words; once complete, the input values' bits (junction applied)
+    bool have = true;
+    // the input buffer: K values, or 2K for a two-half input (loads past it read 0)
+    const __amdgpu_buffer_rsrc_t ir =
+        p_rsrc(xm >= 4 ? a.ws + L.in_off : a.ws, (size_t)(xm >= 5 ? 2 * K : K) * sizeof(float));
+    const uint32_t to = (uint32_t)t * 4u;
+    // The whole offset goes in the per-lane operand: the range check (a load past the
+    // buffer returns 0 and makes no memory request) leaves the scalar offset out.
+    auto issue = [&]() {
+        if (xm >= 5) {
+            const uint32_t th = to + (uint32_t)K * 4u;
+#pragma unroll
+            for (int i = 0; i < NE / 2; ++i) {
+                u[i] = __builtin_amdgcn_raw_buffer_load_b32(ir, to + (uint32_t)(i * kPThreads * 4), 0, kCpolSc1);
+                u[NE / 2 + i] =
+                    __builtin_amdgcn_raw_buffer_load_b32(ir, th + (uint32_t)(i * kPThreads * 4), 0, kCpolSc1);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NE; ++i)
+                u[i] = __builtin_amdgcn_raw_buffer_load_b32(ir, to + (uint32_t)(i * kPThreads * 4), 0, kCpolSc1);
+        }
+    };
+    const int nv = (K + kPThreads - 1) / kPThreads;  // element slots in use (wave-uniform)
+    // every element this thread holds has arrived: convert (junction applied) in place
+    auto check = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NE / 2; ++i) {
+            if (i >= nv) break;
+            const bool mine = t + i * kPThreads < K;
+            if (mine && (u[i] == kPending || (xm >= 5 && u[NE / 2 + i] == kPending))) ok = false;
+        }
+        if (xm == 4) {
+#pragma unroll
+            for (int i = NE / 2; i < NE; ++i) {
+                if (i >= nv) break;
+                if (t + i * kPThreads < K && u[i] == kPending) ok = false;
+            }
+        }
+        have = ok;
+        if (!ok || xm == 4) return;
+#pragma unroll
+        for (int i = 0; i < NE / 2; ++i) {
+            if (i >= nv) break;
+            const float lo = __uint_as_float(u[i]), hi = __uint_as_float(u[NE / 2 + i]);
+            float h;
+            if (xm == 5) {
+                h = __fadd_rn(lo, hi);
+            } else {
+                const float r = lo > 0.0f ? lo : 0.0f;
+                h = __fmul_rn(__fmul_rn(r, r), hi);
+            }
+            u[i] = __float_as_uint(h);
+        }
+    };
+    if (!part) return true;
+    const PWAddr cad = p_weight_addr(L, wg, w);
+    PWeights cur;
+    __builtin_amdgcn_sched_barrier(0);
+    if (xm >= 4) issue();
+    __builtin_amdgcn_sched_barrier(0);
+    p_load_weights(cad, l, cur);  // a fixed count: the check of the input waits for the input alone
+    __builtin_amdgcn_sched_barrier(0);
+    if (xm < 4) {  // the caller's input (first layer): ready, ordinary loads
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            if (i >= nv) break;
+            const int k = min(t + i * kPThreads, K - 1);
+            u[i] = xm == 0 ? (uint32_t) static_cast<const uint16_t *>(a.x)[k] << 16
+                           : static_cast<const uint32_t *>(a.x)[k];
+        }
+    } else {
+        check();
+    }
+
+    // (2) until every value of the input has arrived: a double-buffered vote in LDS
+    //     behind LDS-only barriers.  A workgroup that produced part of the previous layer
+    //     is on time and asks again at once; one that had no work there may be waiting
+    //     layers early and first waits cheaply (below).
+    const bool on_time = li > 0 && wg < p_entry(a.table, li - 1).nwg;
+    int rounds = 0;
+    for (int par = 0;; par ^= 1) {
+        const uint64_t b = __ballot(!have);
+        if (l == 0) vote[par * kPWaves + w] = b != 0;
+        lds_barrier();
+        uint32_t any = 0;
+#pragma unroll
+        for (int i = 0; i < kPWaves; ++i) any |= vote[par * kPWaves + i];
+        if (!any) break;
+        if (++rounds >= a.spin_limit) {
+            if (t == 0) __hip_atomic_store(a.status, li + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        // Not there yet.  A workgroup with no work in the layers before may be waiting
+        // several layers early: until the first 64 values have arrived (their producer
+        // finishes with the others), only wave 0 asks, one line per poll and at most
+        // kPCheapPolls times, while the other waves wait at the barrier.
+        if (!on_time && w == 0) {
+            for (int c = 0; c < kPCheapPolls; ++c) {
+                const uint32_t v0 = __builtin_amdgcn_raw_buffer_load_b32(ir, (uint32_t)l * 4u, 0, kCpolSc1);
+                if (__ballot(l < K && v0 == kPending) == 0) break;
+            }
+        }
+        lds_barrier();
+        if (!have) {
+            issue();
+            check();
+        }
+    }
+
+    // (3) per-token absmax over the whole input, then each element -> int8 in LDS: the
+    //     arithmetic of quantize8 (one fp32 multiply, then the add of 1.5 * 2^23 that rounds
+    //     half to even; the code is the sum's low byte)
+    const int ne = xm >= 5 ? min(nv, NE / 2) : nv;  // element slots holding input values
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        if (i >= ne) break;
+        if (t + i * kPThreads < K) mx = fmaxf(mx, fabsf(__uint_as_float(u[i])));
+    }
+    mx = wave_max(mx);
+    if (l == 0) amax_part[w] = mx;
+    lds_barrier();
+    uint32_t um = 0;
+#pragma unroll
+    for (int i = 0; i < kPWaves; ++i) um = max(um, __float_as_uint(amax_part[i]));
+    const float amax_c = fmaxf(__uint_as_float(um), 1e-5f);
+    const float inv = __fdiv_rn(127.0f, amax_c);
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            if (i >= ne) break;
+            const int k = t + i * kPThreads;
+            if (k < K) {
+                const float v = __uint_as_float(u[i]) * inv;
+                qs[k] = (int8_t)(__float_as_uint(v + 12582912.0f) & 0xFFu);
+            }
+        }
+    }
+    const float s_a = __fdiv_rn(amax_c, 127.0f);
+    lds_barrier();
+
+    // (4) this wave's blocks of its tile: matrix-core steps on the LDS copy of q (token 0
+    //     in lanes 0..15, the other lanes zero) and the decoded weights in `cur`
+    bool active;
+    int tile, b0, nb;
+    p_role(L, wg, w, &active, &tile, &b0, &nb);
+    const int g = l >> 4, j = l & 15;
+    const int ti = w / L.nw, wv = w - ti * L.nw;
+    float yacc = 0.0f;
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < kPMaxNB; ++i) {
+            if (i < nb) {
+                v4i a0 = v4i{0, 0, 0, 0}, a1 = v4i{0, 0, 0, 0};
+                if (j == 0) {
+                    const int8_t *qp = qs + (size_t)(b0 + i) * kBlockK + g * 16;
+                    a0 = *reinterpret_cast<const v4i *>(qp);
+                    a1 = *reinterpret_cast<const v4i *>(qp + 64);
+                }
+                v4i c = v4i{0, 0, 0, 0};
+                c = mfma_i8(a0, decode16(cur.w[i].x), c);
+                c = mfma_i8(a1, decode16(cur.w[i].y), c);
+                yacc = fmaf(cur.s[i], (float)c[0], yacc);
+            }
+        }
+        red[w * kWave + l] = yacc;
+    }
+    lds_barrier();
+
+    // (5) wave 0 of each tile adds its waves' partials in wave order and stores the 16 rows
+    if (active && wv == 0 && g == 0) {
+        const int nblk = K >> 7;
+        const int used = (nblk + L.per - 1) / L.per;
+        float sum = 0.0f;
+        for (int ww = 0; ww < used; ++ww) sum += red[(ti * L.nw + ww) * kWave + j];
+        const float yv = sum * (s_a * 0.015625f);
+        const int row = tile * (int)kTileN + j;
+        if (li != a.withhold) {
+            if (L.out_off < 0) a.y[row] = yv;
+            else st_agent(reinterpret_cast<float *>(a.ws + L.out_off) + row, yv);
+        }
+    }
+    return true;
+}
+
+__global__ __launch_bounds__(kPThreads) void chain_persistent_kernel(PArgs a) {
+    __shared__ __align__(16) int8_t qs[kPMaxK];
+    __shared__ float red[kPWaves * kWave];
+    __shared__ uint32_t vote[2 * kPWaves];
+    __shared__ float amax_part[kPWaves];
+    for (int li = 0; li < a.n; ++li)
+        if (!p_layer(a, li, qs, red, vote, amax_part)) return;
+}
+
+// Fills the workspace's layer buffers with the pending pattern and clears the status word.
+__global__ void chain_persistent_fill(uint4 *p, size_t n16, int *status) {
+    const uint4 v = make_uint4(kPending, kPending, kPending, kPending);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+}
+
+// Host side: geometry per layer and the workspace layout.
+constexpr int kPTableAlign = 256;
+
+bitnet_status_t persist_plan(const bitnet_chain_layer_t *layers, int n, int M, int xdt, int64_t cus, PLayer *out,
+                             size_t *ws_bytes, int *grid) {
+    if (!layers || n < 1) return BITNET_ERR_INVALID_ARG;
+    if (M != 1) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
+    ChainPlan cp;
+    const bitnet_status_t st = chain_plan(layers, n, M, layers[0].K, &cp);
+    if (st != BITNET_OK) return st;
+    if (cus < 1) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    size_t off = kPTableAlign;  // the status word lives in the first 256 bytes
+    int g = 0;
+    for (int i = 0; i < n; ++i) {
+        const bitnet_chain_layer_t &Lc = layers[i];
+        PLayer p{};
+        p.packed = Lc.packed;
+        p.scales = Lc.scales;
+        p.N = Lc.N;
+        p.K = Lc.K;
+        if (Lc.K > kPMaxK || (Lc.fold_input && Lc.K > kPMaxK / 2)) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        // weights and scales are read through 32-bit buffer ranges
+        if ((size_t)Lc.N * Lc.K / 4 > (size_t)0x7FFFFFF0u) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        const int nblk = Lc.K / (int)kBlockK, tiles = Lc.N / (int)kTileN;
+        p.tp = 0;
+        for (int tp = 4; tp >= 1; tp >>= 1) {
+            const int nw = kPWaves / tp, per = (nblk + nw - 1) / nw;
+            const int64_t nwg = (tiles + tp - 1) / tp;
+            if (per <= kPMaxNB && nwg <= cus) {
+                p.tp = tp;
+                p.nw = nw;
+                p.per = per;
+                p.nwg = (int)nwg;
+                break;
+            }
+        }
+        if (p.tp == 0) return BITNET_ERR_UNSUPPORTED_SHAPE;
+        g = p.nwg > g ? p.nwg : g;
+        if (i == 0) {
+            p.xm = xdt == BITNET_DT_BF16 ? 0 : 1;
+            p.in_off = -1;
+        } else {
+            p.xm = Lc.fold_input == BITNET_JUNCTION_SUM ? 5 : Lc.fold_input == BITNET_JUNCTION_RELU2_GLU ? 6 : 4;
+            p.in_off = out[i - 1].out_off;
+        }
+        if (i == n - 1) {
+            p.out_off = -1;
+        } else {
+            p.out_off = (int64_t)off;
+            off += align256((size_t)Lc.N * sizeof(float));
+        }
+        out[i] = p;
+    }
+    *ws_bytes = off;
+    *grid = g;
+    return BITNET_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t bitnet_w2a8_persist_table_bytes(int n) { return n < 1 ? 0 : (size_t)n * sizeof(PLayer); }
+
+bitnet_status_t bitnet_w2a8_persist_prepare(const bitnet_chain_layer_t *layers, int n, int M, int xdt, int64_t cus,
+                                            void *table_host, size_t table_bytes, size_t *workspace_bytes) {
+    if (!table_host || !workspace_bytes || n < 1 || table_bytes < (size_t)n * sizeof(PLayer) || cus < 0)
+        return BITNET_ERR_INVALID_ARG;
+    if (cus == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return BITNET_ERR_HIP;
+        cus = c;
+    }
+    int grid = 0;
+    return persist_plan(layers, n, M, xdt, cus, static_cast<PLayer *>(table_host), workspace_bytes, &grid);
+}
+
+bitnet_status_t bitnet_w2a8_chain_persistent_ex(const void *table_dev, int n, const void *x, int xdt, int M, float *y,
+                                                void *workspace, size_t workspace_bytes, int spin_limit,
+                                                int withhold_layer, hipStream_t stream) {
+    if (!table_dev || n < 1 || !x || !y || !workspace || !aligned(table_dev, 16) || !aligned(x, 16) ||
+        !aligned(y, 16) || !aligned(workspace, 256) || spin_limit < 0)
+        return BITNET_ERR_INVALID_ARG;
+    if (xdt != BITNET_DT_BF16 && xdt != BITNET_DT_F32) return BITNET_ERR_INVALID_ARG;
+    if (M != 1) return BITNET_ERR_UNSUPPORTED_SHAPE;
+    const DeviceSlots dev = device_slots(stream);
+    if (dev.cus < 1) return BITNET_ERR_HIP;
+    if (workspace_bytes < (size_t)kPTableAlign) return BITNET_ERR_INVALID_ARG;
+    PArgs a;
+    a.table = static_cast<const PLayer *>(table_dev);
+    a.n = n;
+    a.x = x;
+    a.y = y;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.ws_bytes = (int64_t)workspace_bytes;
+    a.status = reinterpret_cast<int *>(workspace);
+    a.spin_limit = spin_limit > 0 ? spin_limit : (1 << 16);  // rounds of up to 64 polls: seconds
+    a.withhold = withhold_layer;
+    const size_t n16 = (workspace_bytes - kPTableAlign) / 16;
+    hipLaunchKernelGGL(chain_persistent_fill, dim3(256), dim3(256), 0, stream,
+                       reinterpret_cast<uint4 *>(a.ws + kPTableAlign), n16, a.status);
+    // one workgroup per CU: every workgroup is resident at once, so every wait is on a
+    // workgroup that is running
+    hipLaunchKernelGGL(chain_persistent_kernel, dim3((unsigned)dev.cus), dim3(kPThreads), 0, stream, a);
+    return launched();
+}
+
+bitnet_status_t bitnet_w2a8_chain_persistent(const void *table_dev, int n, const void *x, int xdt, int M, float *y,
+                                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return bitnet_w2a8_chain_persistent_ex(table_dev, n, x, xdt, M, y, workspace, workspace_bytes, 0, -1, stream);
+}
+
+}  // extern "C"

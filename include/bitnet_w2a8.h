@@ -330,6 +330,60 @@ size_t bitnet_w2a8_chain_static_max_bytes(void);
 bitnet_status_t bitnet_w2a8_chain_static(const bitnet_chain_layer_t *layers, int n, const void *x, int xdt, int M,
                                          float *y, hipStream_t stream);
 
+/* The decode pass of bitnet_w2a8_chain at batch 1 as ONE launch (a persistent form, an
+ * experiment beside the launch-per-layer chain): the same operation ([P2] "Architecture
+ * foundations": W2A8 products; [P3] "Why WASM": a 2.4B ternary model decoded token by
+ * token; the junctions of [P4] "BitRun v0.2 measured"), the same per-layer arithmetic
+ * (quantisation exactly as bitnet_quant_act / _fold / _relu2_glu, int32 block sums, one
+ * fp32 scale per block), within the fp32 bound of the products called one by one.  One
+ * 1024-thread workgroup per compute unit runs every layer; a layer's output goes to the
+ * workspace with device-coherent stores and the next layer's workgroups poll it (each
+ * value starts as a pending pattern), so no launch separates the layers.  Every wait is
+ * bounded: a wait that gives up records its layer in the workspace's status word and its
+ * workgroup ends, so the launch always completes.  On this device it is slower than
+ * bitnet_w2a8_chain (the exchange between layers costs more than a launch).
+ *
+ * bitnet_w2a8_persist_table_bytes(n): bytes of the layer table for n layers (0 if n < 1).
+ *
+ * bitnet_w2a8_persist_prepare: plans the layers into table_host (host memory, at least
+ * bitnet_w2a8_persist_table_bytes(n)) and returns the workspace size the launch needs.
+ *   layers, n   as bitnet_w2a8_chain (device pointers inside; they must stay valid while
+ *               the table is used)
+ *   M           1 (else BITNET_ERR_UNSUPPORTED_SHAPE)
+ *   xdt         BITNET_DT_BF16 or BITNET_DT_F32, the type of the first layer's input
+ *   cus         compute units of the device that will run it; 0 = the current device's
+ *   Rules: as bitnet_w2a8_chain, and each K <= 16384 (<= 8192 behind a junction); a layer
+ *   must fit in `cus` workgroups (else BITNET_ERR_UNSUPPORTED_SHAPE).
+ * The caller copies the table, byte for byte, into device memory (16-byte aligned) and
+ * passes that copy to the launches below.
+ *
+ * bitnet_w2a8_chain_persistent: one pass.
+ *   table_dev        device, the prepared table of n layers
+ *   x                device, [1][K of layer 0] of xdt (the type given to prepare)
+ *   y                device, fp32 [1][N of the last layer] (out)
+ *   workspace        device, 256-byte aligned, at least the prepared size; clobbered.
+ *                    After the launch: int32 status at offset 0 (0 success; i + 1 when a
+ *                    wait for layer i's input gave up; -(i + 1) when layer i of the table
+ *                    does not fit the workspace or its shape fields are invalid, found
+ *                    before anything of layer i is written), and each intermediate
+ *                    layer's fp32 output at its planned offset.
+ * Returns BITNET_OK once both launches (a fill of the workspace, then the pass) are
+ * enqueued on `stream`; the status word is the pass's own result.  Capturable in a HIP
+ * graph; no allocation.  Launches that overlap on one device with work that keeps compute
+ * units busy can make the waits give up (status > 0), never hang.
+ *
+ * bitnet_w2a8_chain_persistent_ex: the same with two test knobs: spin_limit (0 = the
+ * default of 65536 poll rounds) bounds every wait; withhold_layer (-1 = none) is a layer
+ * whose output is never stored, so that the waits for it give up. */
+size_t bitnet_w2a8_persist_table_bytes(int n);
+bitnet_status_t bitnet_w2a8_persist_prepare(const bitnet_chain_layer_t *layers, int n, int M, int xdt, int64_t cus,
+                                            void *table_host, size_t table_bytes, size_t *workspace_bytes);
+bitnet_status_t bitnet_w2a8_chain_persistent(const void *table_dev, int n, const void *x, int xdt, int M, float *y,
+                                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+bitnet_status_t bitnet_w2a8_chain_persistent_ex(const void *table_dev, int n, const void *x, int xdt, int M, float *y,
+                                                void *workspace, size_t workspace_bytes, int spin_limit,
+                                                int withhold_layer, hipStream_t stream);
+
 /* Exact integer product acc[m][n] = sum_k T[n][k] * Q[m][k] (int32, device, [M][N]),
  * computed by the same kernels as the two products above (M <= 16: the decode
  * kernel; larger M: the prefill kernel), so that their integer core can be

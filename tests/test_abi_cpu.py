@@ -433,3 +433,59 @@ def test_other_wrappers_check_their_outputs():
                                 acc=torch.zeros((1, 16), dtype=torch.int32))
     with pytest.raises(ValueError, match="sink"):
         bn.bitnet_probe_stream_read(torch.zeros(4096, dtype=torch.uint8), sink=torch.zeros(0, dtype=torch.int32))
+
+
+# The one-launch (persistent) chain: its host-side plan chooses, per layer, the row tiles
+# per workgroup (4, 2 or 1: as few workgroups as fit), the waves per tile and blocks per
+# wave, and lays out one output buffer per layer after a 256-byte status block.
+def _plan(shapes, folds, M=1, xdt=0, cus=256):
+    n = len(shapes)
+    arr = (bn.ChainLayer * n)()
+    for i, ((N, K), f) in enumerate(zip(shapes, folds)):
+        arr[i] = bn.ChainLayer(0x100000, 0x200000, N, K, f)
+    nb = bn.lib().bitnet_w2a8_persist_table_bytes(n)
+    host = np.zeros(nb, np.uint8)
+    ws = ctypes.c_size_t(0)
+    st = bn.lib().bitnet_w2a8_persist_prepare(ctypes.cast(arr, ctypes.c_void_p), n, M, xdt, cus,
+                                               host.ctypes.data_as(ctypes.c_void_p), nb, ctypes.byref(ws))
+    return st, host.view(np.int32).reshape(n, 16), ws.value
+
+
+def test_persistent_plan_of_the_stack_layers():
+    shapes = [(2560, 2560)] * 4 + [(13824, 2560), (2560, 6912)]
+    folds = [0, 0, 0, 0, 0, 1]
+    st, t, ws = _plan(shapes, folds)
+    assert st == bn.BITNET_OK
+    assert bn.lib().bitnet_w2a8_persist_table_bytes(6) == 6 * 64
+    # int32 fields after the pointers and offsets: N, K, xm, tp, nw, per, nwg
+    fields = [tuple(row[8:15]) for row in t]
+    assert fields[0] == (2560, 2560, 0, 4, 4, 5, 40)       # bf16 input, 4 tiles x (4 waves x 5 blocks)
+    assert fields[1] == (2560, 2560, 4, 4, 4, 5, 40)       # previous output
+    assert fields[4] == (13824, 2560, 4, 4, 4, 5, 216)     # 864 tiles on 216 workgroups
+    assert fields[5] == (2560, 6912, 5, 2, 8, 7, 80)       # folded input: 2 tiles x (8 waves x 7 blocks)
+    offs = t.view(np.int64).reshape(6, 8)
+    assert list(offs[:, 2]) == [-1, 256, 256 + 10240, 256 + 20480, 256 + 30720, 256 + 40960]  # inputs
+    assert list(offs[:, 3]) == [256, 256 + 10240, 256 + 20480, 256 + 30720, 256 + 40960, -1]   # outputs
+    assert ws == 256 + 4 * 10240 + 55296
+    # the squared-ReLU gate is its own input form
+    _, t2, _ = _plan(shapes, [0, 0, 0, 0, 0, 2])
+    assert t2[5][10] == 6
+
+
+def test_persistent_plan_rejections():
+    ok = [(256, 512), (384, 256)]
+    assert _plan(ok, [0, 0])[0] == bn.BITNET_OK
+    assert _plan(ok, [0, 0], M=2)[0] == bn.BITNET_ERR_UNSUPPORTED_SHAPE      # batch 1 only
+    assert _plan(ok, [0, 0], xdt=2)[0] == bn.BITNET_ERR_INVALID_ARG          # bf16 or fp32 input
+    assert _plan([(256, 512), (512, 384)], [0, 0])[0] == bn.BITNET_ERR_UNSUPPORTED_SHAPE  # K != previous N
+    assert _plan([(16384, 128), (128, 8192 + 128)], [0, 1])[0] == bn.BITNET_ERR_UNSUPPORTED_SHAPE  # junction K > 8192
+    assert _plan([(256, 16384 + 128)], [0])[0] == bn.BITNET_ERR_UNSUPPORTED_SHAPE   # K > 16384
+    assert _plan([(2560, 2560)], [0], cus=16)[0] == bn.BITNET_ERR_UNSUPPORTED_SHAPE  # 40 workgroups > 16 CUs
+    assert _plan([(2560, 2560)], [0], cus=40)[0] == bn.BITNET_OK
+    L = bn.lib()
+    assert L.bitnet_w2a8_chain_persistent(_FAKE, 2, _FAKE, 0, 2, _FAKE, _FAKE, 4096, _NULL) == \
+        bn.BITNET_ERR_UNSUPPORTED_SHAPE
+    assert L.bitnet_w2a8_chain_persistent(_FAKE, 2, _MIS, 0, 1, _FAKE, _FAKE, 4096, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_chain_persistent(_FAKE, 2, _FAKE, 3, 1, _FAKE, _FAKE, 4096, _NULL) == bn.BITNET_ERR_INVALID_ARG
+    assert L.bitnet_w2a8_chain_persistent_ex(_FAKE, 2, _FAKE, 0, 1, _FAKE, _FAKE, 4096, -1, -1, _NULL) == \
+        bn.BITNET_ERR_INVALID_ARG

@@ -1,0 +1,191 @@
+"""GPU parity of the one-launch (persistent) decode chain, bitnet_w2a8_chain_persistent.
+
+Every layer's output stays in the workspace after the launch, so each product is
+checked element by element against the oracle fed the GPU's own input to it (the
+layer-local parity of the launch-per-layer chain), and each requantisation against the
+oracle's own decision (R11 with identical inputs).  Also: graph capture and replay, and
+the bounded waits giving up when the host withholds a layer's output (every kernel still
+ends)."""
+import numpy as np
+import pytest
+
+import bit_gemv_i2_amd as bn
+import oracle
+import oracle_pool as op
+import parity_stats
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+# (N, K, junction in front); K of a layer behind a junction is half the previous N
+SMALL = [(256, 512, False), (384, 256, False), (1024, 384, False), (384, 512, True), (2304, 384, False),
+         (272, 1152, True)]
+
+
+def _chain(seed, junction):
+    ws, Ts, Ss = [], [], []
+    for i, (N, K, f) in enumerate(SMALL):
+        r = wl.rng_for(81, seed, i)
+        T = wl.ternary_uniform(r, N, K)
+        S = wl.uniform_scales(r, N, K, div=np.sqrt(7 * K / 6))
+        Ts.append(T)
+        Ss.append(S)
+        ws.append(bn.PackedWeight.from_ternary(T, S))
+    return bn.Chain(ws, [junction if f else False for (_, _, f) in SMALL]), Ts, Ss
+
+
+def _x(K, seed, xdt):
+    xb = wl.normal_act(wl.rng_for(82, seed), 1, K)
+    if xdt == "bf16":
+        return xb, torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    x = wl.bf16_to_f32(xb) * np.float32(0.75)
+    return x, torch.from_numpy(x).cuda()
+
+
+def _check_layers(chain, Ts, Ss, junction, xin, xdt, outs, y):
+    prev = None
+    for k, (N, K, f) in enumerate(SMALL):
+        if k == 0:
+            q, s = oracle.quant_act_bf16(xin) if xdt == "bf16" else oracle.quant_act_f32(xin)
+        elif f:
+            q, s = oracle.fold_quant(prev) if junction == "sum" else oracle.glu_quant(prev)
+        else:
+            q, s = oracle.quant_act_f32(prev)
+        ref = oracle.w2a8(oracle.pack_i2s(Ts[k]), Ss[k], q, s, N, K)
+        got = outs[k] if k < len(SMALL) - 1 else y
+        parity_stats.record(got, ref["y64"], ref["mag"])
+        ratio, bad, _ = op.f32_check(got, ref["y64"], ref["mag"])
+        assert bad == 0, f"layer {k}: {bad} outputs outside the tolerance (worst {ratio:.3g}x)"
+        prev = got
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("junction", ["sum", "relu2_glu"])
+def test_persistent_chain_every_layer_against_the_oracle(gpu, junction, xdt):
+    chain, Ts, Ss = _chain(1, junction)
+    xin, x = _x(SMALL[0][1], 2, xdt)
+    y = chain.persistent(x)
+    torch.cuda.synchronize()
+    bxdt = bn.BITNET_DT_BF16 if xdt == "bf16" else bn.BITNET_DT_F32
+    outs, status = chain.persistent_layer_outputs(1, bxdt)
+    assert status == 0
+    _check_layers(chain, Ts, Ss, junction, xin, xdt, outs, y.cpu().numpy())
+    # a second call on the same workspace (refilled before the launch) gives the same result
+    y2 = chain.persistent(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+
+
+def test_persistent_chain_graph_replays(gpu):
+    chain, Ts, Ss = _chain(3, "sum")
+    K0 = SMALL[0][1]
+    xs = [_x(K0, 10 + i, "bf16")[1] for i in range(4)]
+    eager = []
+    for x in xs:
+        eager.append(chain.persistent(x).cpu().numpy())
+    xbuf = torch.empty_like(xs[0])
+    ybuf = torch.empty((1, SMALL[-1][0]), dtype=torch.float32, device="cuda")
+    xbuf.copy_(xs[0])
+    chain.persistent(xbuf, y=ybuf)  # plan, table and workspace exist before the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain.persistent(xbuf, y=ybuf)
+    for i, x in enumerate(xs):
+        xbuf.copy_(x)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(ybuf.cpu().numpy().view(np.uint32), eager[i].view(np.uint32)), f"replay {i}"
+        assert chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)[1] == 0
+
+
+def test_persistent_chain_bounded_wait_gives_up(gpu):
+    """The host withholds layer 2's output (test-only knob) and sets a tiny spin limit:
+    the workgroups waiting for it give up, record the layer in the status word and end;
+    the launch completes.  A normal launch afterwards is correct again."""
+    chain, Ts, Ss = _chain(5, "sum")
+    xin, x = _x(SMALL[0][1], 6, "bf16")
+    chain.persistent(x, spin_limit=64, withhold=2)
+    torch.cuda.synchronize()
+    _, status = chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)
+    assert status >= 4, status  # layer 3 (or a later one) gave up: status = its index + 1
+    y = chain.persistent(x)
+    torch.cuda.synchronize()
+    outs, status = chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)
+    assert status == 0
+    _check_layers(chain, Ts, Ss, "sum", xin, "bf16", outs, y.cpu().numpy())
+
+
+def test_persistent_chain_stops_on_a_table_that_does_not_fit_the_workspace(gpu):
+    """The caller declares a workspace 4 bytes short of the plan (the buffer itself is
+    whole, so nothing could land outside it): every workgroup stops at the first layer
+    whose output would not fit, the status word says which (negative), nothing past the
+    declared size is written, and the launch ends."""
+    chain, _, _ = _chain(9, "sum")
+    _, x = _x(SMALL[0][1], 10, "bf16")
+    plan = chain.plan_persistent(1, bn.BITNET_DT_BF16)
+    ws = torch.full((plan.workspace_bytes + 256,), 0x5A, dtype=torch.uint8, device="cuda")
+    y = torch.zeros((1, SMALL[-1][0]), dtype=torch.float32, device="cuda")
+    short = plan.workspace_bytes - 4
+    st = bn.lib().bitnet_w2a8_chain_persistent(plan.table.data_ptr(), plan.n, x.data_ptr(), bn.BITNET_DT_BF16, 1,
+                                               y.data_ptr(), ws.data_ptr(), short,
+                                               torch.cuda.current_stream().cuda_stream)
+    assert st == bn.BITNET_OK
+    torch.cuda.synchronize()
+    host = ws.cpu().numpy()
+    # the last intermediate output (layer n - 2) ends exactly at the plan's size
+    assert int(host[:4].view(np.int32)[0]) == -(plan.n - 1)
+    assert (host[short:] == 0x5A).all()
+    assert (y.cpu().numpy() == 0).all()
+
+
+def test_persistent_chain_rejects_batches_above_one(gpu):
+    chain, _, _ = _chain(7, "sum")
+    x = torch.zeros((2, SMALL[0][1]), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bn.BitnetError) as ei:
+        chain.persistent(x)
+    assert ei.value.status == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("junction", ["sum", "relu2_glu"])
+def test_persistent_stack_30_layers_every_product(gpu, junction):
+    """The 30-layer stack in one launch at batch 1: all 180 products element by element
+    against the oracle fed the GPU's own input, and the requantisation decisions."""
+    ws = []
+    for layer in range(wl.STACK_LAYERS):
+        for idx in range(6):
+            T, S = wl.stack_matrix(layer, idx)
+            ws.append(bn.PackedWeight.from_ternary(T, S))
+    n = len(ws)
+    chain = bn.Chain(ws, [junction if i % 6 == 5 else False for i in range(n)])
+    xb = wl.stack_input(1)
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    y = chain.persistent(x)
+    torch.cuda.synchronize()
+    outs, status = chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)
+    assert status == 0
+    outs = outs + [y.cpu().numpy()]
+    tasks = []
+    for p in range(n):
+        layer, idx = divmod(p, 6)
+        kind = "bf16" if p == 0 else (junction if idx == 5 else "plain")
+        nxt = None if p == n - 1 else (junction if idx == 4 else "plain")
+        tasks.append((p, layer, idx, kind, nxt, [(1, xb if p == 0 else outs[p - 1], outs[p])]))
+    print(f"persistent stack {junction}: oracle on {n} products in {op.workers()} processes", flush=True)
+    with op.pool() as ex:
+        res = [r for chunk in ex.map(op.stack_product, tasks, chunksize=3) for r in chunk]
+    assert len(res) == n
+    codes = sum(r["codes"] for r in res)
+    flips = sum(r["n_diff"] for r in res)
+    print(f"persistent stack {junction}: worst error / bound {max(r['ratio'] for r in res):.3f}, plain max "
+          f"relative error {max(r['plain_rel'] for r in res):.3e}, requantisation codes at a midpoint that "
+          f"differ {flips} of {codes}", flush=True)
+    parity_stats.note(f"persistent stack {junction}", max(r["ratio"] for r in res), max(r["plain_rel"] for r in res))
+    for r in res:
+        where = f"{junction} product {r['p']}"
+        assert r["bad"] == 0, f"{where}: {r['bad']} outputs outside the tolerance (worst {r['ratio']:.3g}x)"
+        assert r["unjustified"] == 0 and r["max_dq"] <= 1, where
+        assert r["n_diff"] <= max(1, r["codes"] // 1000), where
