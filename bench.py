@@ -51,8 +51,8 @@ ROTATE_BYTES = 2 * LLC_BYTES
 # for a 64 MiB device copy (FETCH_SIZE x 1.999, WRITE_SIZE x 1.000).  Valid only
 # for the kernel source it was taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha1": "6e91de8415553fc052f67f1b6c5595916af4366f",
-    "fused": {"bytes_per_launch": 10104986, "fetch_kib": 4909.0, "write_kib": 54.0},
+    "kernel_source_sha1": "c8f9f93c7838589dd6a845f9c68daf87440c151b",
+    "fused": {"bytes_per_launch": 10092703, "fetch_kib": 4903.0, "write_kib": 54.0},
     "product": {"bytes_per_launch": 10076325, "fetch_kib": 4895.0, "write_kib": 54.0},
     "fetch_scale": 1.999, "write_scale": 1.000,
 }
@@ -361,10 +361,18 @@ def stack_shape(torch, bn, wl, runs=((1, "sum"), (8, "sum"), (1, "relu2_glu")), 
         y = torch.empty((M, wl.STACK_HIDDEN), dtype=torch.float32, device="cuda")
         chain.workspace(M)
         us = graph_us_per_launch(torch, lambda i: chain(x, y=y), 1, reps)
-        out.append({"shape": "stack_30x6_decode", "M": M, "junction": junction, "token_step_us": us,
-                    "tokens_per_s": M * 1e6 / us, "products_per_token": len(ws), "packed_bytes_per_token": pbytes,
-                    "packed_GBps": pbytes / us / 1e3, "pct_hbm_packed": 100.0 * pbytes / us / 1e3 / HBM_PEAK_GBS,
-                    "setup_s": setup_s})
+        row = {"shape": "stack_30x6_decode", "M": M, "junction": junction, "token_step_us": us,
+               "tokens_per_s": M * 1e6 / us, "products_per_token": len(ws), "packed_bytes_per_token": pbytes,
+               "packed_GBps": pbytes / us / 1e3, "pct_hbm_packed": 100.0 * pbytes / us / 1e3 / HBM_PEAK_GBS,
+               "setup_s": setup_s}
+        if M == 1:  # the one-launch persistent form of the same token (plan and workspace made eagerly first)
+            chain.persistent(x, y=y)
+            torch.cuda.synchronize()
+            pus = graph_us_per_launch(torch, lambda i: chain.persistent(x, y=y), 1, reps)
+            torch.cuda.synchronize()
+            row["persistent_token_step_us"] = pus
+            row["persistent_status"] = chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)[1]
+        out.append(row)
         del chain
     del ws
     torch.cuda.empty_cache()
@@ -602,7 +610,8 @@ def calibration_copy(torch):
 def profile_stack(torch, bn, wl):
     """One token of the 30-layer stack (180 products, linear fold) captured as a graph,
     replayed 5 times at batch 1 and 5 times at batch 8, with a synchronisation after
-    every replay so each token stands alone in the trace."""
+    every replay so each token stands alone in the trace; at batch 1 also the same token
+    as one persistent launch (bitnet_w2a8_chain_persistent), replayed 5 times."""
     ws = []
     for layer in range(wl.STACK_LAYERS):
         for idx in range(6):
@@ -618,7 +627,18 @@ def profile_stack(torch, bn, wl):
             g.replay()
             torch.cuda.synchronize()
         log(f"profile stack: batch {M}, 5 token replays done")
-        del g, chain
+        del g
+        if M == 1:  # the same token as one persistent launch (after its fill launch)
+            chain.persistent(x, y=y)
+            torch.cuda.synchronize()
+            g = capture(torch, lambda i: chain.persistent(x, y=y), 1)
+            for _ in range(5):
+                g.replay()
+                torch.cuda.synchronize()
+            status = chain.persistent_layer_outputs(1, bn.BITNET_DT_BF16)[1]
+            log(f"profile stack: batch 1 persistent, 5 token replays done (status {status})")
+            del g
+        del chain
 
 
 def profile_shapes(torch, bn, wl):
