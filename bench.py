@@ -43,6 +43,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix-core peak, published
 LLC_BYTES = 256 << 20          # Infinity Cache
+HEADLINE_PAIRS = 41            # timed replay pairs behind the headline's median (odd)
 ROTATE_BYTES = 2 * LLC_BYTES
 
 # HBM bytes per launch of the headline kernels (the fused quantise-and-multiply
@@ -706,9 +707,9 @@ def main():
     g_rot = capture(torch, d.fused, d.rot.R)
     whole_replay_ms = time_graph(torch, g, 1, pre=g_rot)
     # `steps` steady-state steps, as the difference of two event-timed graph replays (one
-    # rotation, and the same rotation followed by the `steps` steps): the median of ten
-    diffs = sorted(steps_by_difference(torch, d.fused, args.steps, d.rot.R))
-    total_ms = (diffs[4] + diffs[5]) / 2
+    # rotation, and the same rotation followed by the `steps` steps): the median of 41 pairs
+    diffs = sorted(steps_by_difference(torch, d.fused, args.steps, d.rot.R, reps=HEADLINE_PAIRS))
+    total_ms = diffs[HEADLINE_PAIRS // 2]
     ms_per_step = total_ms / args.steps
     # what one replay of a graph of just the `steps` steps costs beyond them (not in `value`)
     graph_replay_fixed_us = (whole_replay_ms - total_ms) * 1e3
@@ -718,7 +719,7 @@ def main():
     quant_us = graph_us_per_launch(torch, d.quant, 64, 10)
     step2_us = graph_us_per_launch(torch, d.step2, d.rot.R, reps)
     eager_us = eager_us_per_launch(torch, d.fused, min(args.steps, 500))
-    # spread: ten more timed replays of the headline graph (not part of `value`)
+    # spread over the timed pairs (the median is `value`)
     rep_us = [x * 1e3 / args.steps for x in diffs]
     del g, g_rot
     y_headline = d.y.cpu().numpy().copy()
@@ -760,13 +761,13 @@ def main():
                              "each step reads a copy last touched a full rotation earlier); timed as the "
                              "difference of two event-timed replays of HIP graphs, one over a whole rotation "
                              "and one over the same rotation followed by the `steps` steps, so the fixed cost "
-                             "of a graph replay cancels (median of 10 pairs); step_us_whole_replay times one "
+                             "of a graph replay cancels (median of 41 pairs); step_us_whole_replay times one "
                              "replay of a graph of just the `steps` steps instead, that fixed cost "
                              "(graph_replay_fixed_us) included"},
         "graph_replay_fixed_us": graph_replay_fixed_us,
         "step_us_whole_replay": whole_replay_ms * 1e3 / args.steps,
         "step_us": ms_per_step * 1e3,
-        "step_us_repeats": {"n": len(rep_us), "median": (rep_us[4] + rep_us[5]) / 2, "min": rep_us[0],
+        "step_us_repeats": {"n": len(rep_us), "median": rep_us[len(rep_us) // 2], "min": rep_us[0],
                             "max": rep_us[-1]},
         "pct_hbm_packed_step": 100.0 * pbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "quant_us": quant_us,
