@@ -672,8 +672,8 @@ def profile_shapes(torch, bn, wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the product shards by output rows; see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the product would shard by output rows; see the design notes).", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -3,7 +3,7 @@
 Test infrastructure.  The workers are fresh interpreters (spawn) that import
 only numpy, the oracle and the seeded input generators -- never torch or the
 HIP library -- regenerate the seeded weights they need from those generators,
-and return the oracle's verdict on the GPU results they are handed.  Splitting
+and return what the oracle finds for the GPU results they are handed.  Splitting
 the work by output rows or by product changes no result: rows and products
 are independent in the oracle's definition.
 """
