@@ -489,3 +489,61 @@ def test_persistent_plan_rejections():
     assert L.bitnet_w2a8_chain_persistent(_FAKE, 2, _FAKE, 3, 1, _FAKE, _FAKE, 4096, _NULL) == bn.BITNET_ERR_INVALID_ARG
     assert L.bitnet_w2a8_chain_persistent_ex(_FAKE, 2, _FAKE, 0, 1, _FAKE, _FAKE, 4096, -1, -1, _NULL) == \
         bn.BITNET_ERR_INVALID_ARG
+
+
+def _random_valid_chain(rng):
+    n = int(rng.integers(2, 9))
+    shapes, folds = [], []
+    K, fold = 128 * int(rng.integers(1, 129)), 0
+    for i in range(n):
+        last = i == n - 1
+        N = 16 * int(rng.integers(1, 600)) if last else 128 * int(rng.integers(1, 65))
+        shapes.append((N, K))
+        folds.append(fold)
+        if not last:
+            fold = int(rng.integers(0, 3)) if (N % 256 == 0 and N // 2 <= 8192) else 0
+            K = N // 2 if fold else N
+    return shapes, folds
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_persistent_plan_invariants_on_random_chains(seed):
+    """Whatever the chain, the plan covers every row and block, stays within the CU count,
+    takes the most row tiles per workgroup that fit, and lays the layer buffers out without
+    overlap; inputs past the size limits are refused."""
+    rng = np.random.default_rng(np.random.SeedSequence([91, seed]))
+    shapes, folds = _random_valid_chain(rng)
+    cus = int(rng.choice([40, 104, 256, 256, 304]))
+    xdt = int(rng.integers(0, 2))
+    st, t, ws = _plan(shapes, folds, 1, xdt, cus)
+    too_big = any(K > 16384 or (f and K > 8192) for (N, K), f in zip(shapes, folds))
+
+    def fits(tp, N, K):
+        nw, nblk = 16 // tp, K // 128
+        per = -(-nblk // nw)
+        return per <= 8 and -(-(N // 16) // tp) <= cus
+
+    if too_big or not all(any(fits(tp, N, K) for tp in (4, 2, 1)) for N, K in shapes):
+        assert st == bn.BITNET_ERR_UNSUPPORTED_SHAPE
+        return
+    assert st == bn.BITNET_OK
+    offs = t.view(np.int64).reshape(len(shapes), 8)
+    end = 256
+    for i, ((N, K), f) in enumerate(zip(shapes, folds)):
+        Nf, Kf, xm, tp, nw, per, nwg = (int(v) for v in t[i][8:15])
+        assert (Nf, Kf) == (N, K)
+        assert xm == ((0 if xdt == bn.BITNET_DT_BF16 else 1) if i == 0 else {0: 4, 1: 5, 2: 6}[f])
+        assert tp in (1, 2, 4) and nw * tp == 16 and 1 <= per <= 8
+        assert per * nw * 128 >= K                      # the waves of a tile cover every block
+        assert nwg * tp * 16 >= N and (nwg - 1) * tp * 16 < N and nwg <= cus  # rows covered, none idle
+        assert all(not fits(bigger, N, K) for bigger in (4, 2) if bigger > tp)
+        if i == 0:
+            assert offs[i, 2] == -1
+        else:
+            assert offs[i, 2] == offs[i - 1, 3]
+        if i == len(shapes) - 1:
+            assert offs[i, 3] == -1
+        else:
+            assert offs[i, 3] == end and end % 256 == 0
+            end += -(-N * 4 // 256) * 256
+    assert ws == end

@@ -189,3 +189,90 @@ def test_persistent_stack_30_layers_every_product(gpu, junction):
         assert r["bad"] == 0, f"{where}: {r['bad']} outputs outside the tolerance (worst {r['ratio']:.3g}x)"
         assert r["unjustified"] == 0 and r["max_dq"] <= 1, where
         assert r["n_diff"] <= max(1, r["codes"] // 1000), where
+
+
+def _plan_fields(shapes, folds, xdt):
+    """The persistent plan of a chain on this device (layer addresses are not read)."""
+    import ctypes
+    n = len(shapes)
+    arr = (bn.ChainLayer * n)()
+    for i, ((N, K), f) in enumerate(zip(shapes, folds)):
+        arr[i] = bn.ChainLayer(0x100000, 0x200000, N, K, f)
+    nb = bn.lib().bitnet_w2a8_persist_table_bytes(n)
+    host = np.zeros(nb, np.uint8)
+    ws = ctypes.c_size_t(0)
+    st = bn.lib().bitnet_w2a8_persist_prepare(ctypes.cast(arr, ctypes.c_void_p), n, 1, xdt, 0,
+                                               host.ctypes.data_as(ctypes.c_void_p), nb, ctypes.byref(ws))
+    return st, host.view(np.int32).reshape(n, 16)
+
+
+def _random_chain_spec(seed, xdt):
+    """A random chain the device can run in one launch: K up to 16384 (8192 behind a
+    junction), so that 4, 2 and 1 row tiles per workgroup all occur."""
+    r = wl.rng_for(84, seed)
+    while True:
+        n = int(r.integers(3, 7))
+        shapes, folds = [], []
+        K, fold = 128 * int(r.integers(1, 41)), 0
+        for i in range(n):
+            last = i == n - 1
+            N = 16 * int(r.integers(1, 200)) if last else 128 * int(r.integers(1, 129))
+            shapes.append((N, K))
+            folds.append(fold)
+            if not last:
+                fold = int(r.integers(0, 3)) if (N % 256 == 0 and N // 2 <= 8192) else 0
+                K = N // 2 if fold else N
+        st, t = _plan_fields(shapes, folds, xdt)
+        if st == bn.BITNET_OK:
+            return shapes, folds, sorted({int(row[11]) for row in t})
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_persistent_random_chains_against_the_oracle(gpu, seed):
+    """Seeded random chains (shapes, junctions, input type) in one persistent launch: every
+    layer's output element by element against the oracle fed the GPU's own input."""
+    xdt = "bf16" if seed % 2 == 0 else "f32"
+    bxdt = bn.BITNET_DT_BF16 if xdt == "bf16" else bn.BITNET_DT_F32
+    shapes, folds, tiles = _random_chain_spec(seed, bxdt)
+    print(f"seed {seed}: {xdt} input, layers {shapes}, junctions {folds}, row tiles per workgroup {tiles}",
+          flush=True)
+    Ts, Ss, ws = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        r = wl.rng_for(85, seed, i)
+        T = wl.ternary_uniform(r, N, K)
+        S = wl.uniform_scales(r, N, K, div=np.sqrt(7 * K / 6))
+        Ts.append(T)
+        Ss.append(S)
+        ws.append(bn.PackedWeight.from_ternary(T, S))
+    codes = {0: False, 1: "sum", 2: "relu2_glu"}
+    chain = bn.Chain(ws, [codes[f] for f in folds])
+    xin, x = _x(shapes[0][1], 86 + seed, xdt)
+    y = chain.persistent(x)
+    torch.cuda.synchronize()
+    outs, status = chain.persistent_layer_outputs(1, bxdt)
+    assert status == 0
+    prev = None
+    for k, ((N, K), f) in enumerate(zip(shapes, folds)):
+        if k == 0:
+            q, s = oracle.quant_act_bf16(xin) if xdt == "bf16" else oracle.quant_act_f32(xin)
+        elif f == 1:
+            q, s = oracle.fold_quant(prev)
+        elif f == 2:
+            q, s = oracle.glu_quant(prev)
+        else:
+            q, s = oracle.quant_act_f32(prev)
+        ref = oracle.w2a8(oracle.pack_i2s(Ts[k]), Ss[k], q, s, N, K)
+        got = outs[k] if k < len(shapes) - 1 else y.cpu().numpy()
+        parity_stats.record(got, ref["y64"], ref["mag"])
+        ratio, bad, _ = op.f32_check(got, ref["y64"], ref["mag"])
+        assert bad == 0, f"seed {seed} layer {k} ({N}x{K}): {bad} outputs outside the tolerance (worst {ratio:.3g}x)"
+        prev = got
+
+
+def test_persistent_random_chains_cover_every_geometry(gpu):
+    """The seeds above between them put 4, 2 and 1 row tiles on a workgroup."""
+    seen = set()
+    for seed in range(4):
+        bxdt = bn.BITNET_DT_BF16 if seed % 2 == 0 else bn.BITNET_DT_F32
+        seen |= set(_random_chain_spec(seed, bxdt)[2])
+    assert seen == {1, 2, 4}, seen
