@@ -636,11 +636,21 @@ class Chain:
             "bitnet_w2a8_chain_persistent")
         return y
 
-    def persistent_layer_outputs(self, M: int = 1, xdt: int = BITNET_DT_BF16):
+    def persistent_layer_outputs(self, M: int = 1, xdt: int = BITNET_DT_BF16, workspace=None):
         """Host views (fp32 [M][N]) of every intermediate layer's output as the last
-        persistent call left them in the binding's workspace, and the status word."""
+        persistent call left them in its workspace (the caller's, if one was passed to that
+        call, else the binding's), and the status word."""
         plan = self.plan_persistent(M, xdt)
-        ws = self._ws[("persistent_ws", M, xdt)].cpu().numpy()
+        if workspace is None:
+            key = ("persistent_ws", M, xdt)
+            if key not in self._ws:
+                raise ValueError("no persistent call with the binding's workspace has been made for this batch and type")
+            workspace = self._ws[key]
+        import torch
+        _check(workspace, "workspace", torch.uint8)
+        if workspace.numel() < plan.workspace_bytes:
+            raise ValueError(f"workspace must hold at least {plan.workspace_bytes} bytes")
+        ws = workspace.cpu().numpy()
         table = plan.host_table.view(np.int64).reshape(plan.n, 8)  # out_off is the 4th 8-byte field
         outs = []
         for i in range(plan.n - 1):

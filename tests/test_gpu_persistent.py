@@ -77,6 +77,31 @@ def test_persistent_chain_every_layer_against_the_oracle(gpu, junction, xdt):
     assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 
+def test_persistent_chain_with_a_caller_workspace(gpu):
+    """A workspace the caller passes serves the launch and the read-back of the layer
+    outputs; the results equal those of the binding's own workspace bit for bit."""
+    chain, Ts, Ss = _chain(4, "relu2_glu")
+    xin, x = _x(SMALL[0][1], 5, "f32")
+    with pytest.raises(ValueError):
+        chain.persistent_layer_outputs(1, bn.BITNET_DT_F32)  # no call with the binding's workspace yet
+    plan = chain.plan_persistent(1, bn.BITNET_DT_F32)
+    mine = torch.empty(plan.workspace_bytes + 4096, dtype=torch.uint8, device="cuda")
+    y1 = chain.persistent(x, workspace=mine)
+    torch.cuda.synchronize()
+    outs1, st1 = chain.persistent_layer_outputs(1, bn.BITNET_DT_F32, workspace=mine)
+    assert st1 == 0
+    _check_layers(chain, Ts, Ss, "relu2_glu", xin, "f32", outs1, y1.cpu().numpy())
+    y2 = chain.persistent(x)
+    torch.cuda.synchronize()
+    outs2, st2 = chain.persistent_layer_outputs(1, bn.BITNET_DT_F32)
+    assert st2 == 0
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    for a, b in zip(outs1, outs2):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    with pytest.raises(ValueError):
+        chain.persistent_layer_outputs(1, bn.BITNET_DT_F32, workspace=mine[:16])
+
+
 def test_persistent_chain_graph_replays(gpu):
     chain, Ts, Ss = _chain(3, "sum")
     K0 = SMALL[0][1]
