@@ -178,3 +178,46 @@ def test_chain_output_and_workspace_stay_in_bounds(gpu, M, junction):
     gy.check(f"chain y M={M}")
     gw.check(f"chain workspace M={M}")
     same(gy.t, chain(x), "chain")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_static_chain_output_stays_in_bounds(gpu, M):
+    """bitnet_w2a8_chain_static writes only its y (its workspace is the library's own array)."""
+    shapes = [(384, 384), (640, 384), (2304, 640), (272, 1152)]
+    ws = []
+    for i, (N, K) in enumerate(shapes):
+        c = wl.small_case(70 + i, 1, N, K)
+        ws.append(bn.PackedWeight.from_ternary(c.T, (c.S / np.float32(np.sqrt(K))).astype(np.float32)))
+    chain = bn.Chain(ws, [False, False, False, "sum"])
+    x = dev(wl.normal_act(wl.rng_for(7, M), M, 384).view(np.int16)).view(torch.bfloat16)
+    gy = Guarded((M, shapes[-1][0]), torch.float32)
+    st = bn.lib().bitnet_w2a8_chain_static(ctypes.cast(chain._arr, ctypes.c_void_p), len(ws),
+                                           ctypes.c_void_p(x.data_ptr()), bn.BITNET_DT_BF16, M,
+                                           ctypes.c_void_p(gy.t.data_ptr()),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == bn.BITNET_OK
+    gy.check(f"static chain y M={M}")
+    same(gy.t, chain(x), "static chain")
+
+
+@pytest.mark.parametrize("junction", ["sum", "relu2_glu"])
+def test_persistent_chain_output_and_workspace_stay_in_bounds(gpu, junction):
+    """The one-launch chain writes only its y and the prepared size of its workspace."""
+    shapes = [(384, 384), (640, 384), (2304, 640), (272, 1152)]  # 17 tiles last, two-half input in front
+    ws = []
+    for i, (N, K) in enumerate(shapes):
+        c = wl.small_case(80 + i, 1, N, K)
+        ws.append(bn.PackedWeight.from_ternary(c.T, (c.S / np.float32(np.sqrt(K))).astype(np.float32)))
+    chain = bn.Chain(ws, [False, False, False, junction])
+    x = dev(wl.normal_act(wl.rng_for(8, 1), 1, 384).view(np.int16)).view(torch.bfloat16)
+    plan = chain.plan_persistent(1, bn.BITNET_DT_BF16)
+    gw = Guarded((plan.workspace_bytes,), torch.uint8)
+    gy = Guarded((1, shapes[-1][0]), torch.float32)
+    st = bn.lib().bitnet_w2a8_chain_persistent(plan.table.data_ptr(), plan.n, x.data_ptr(), bn.BITNET_DT_BF16, 1,
+                                               gy.t.data_ptr(), gw.t.data_ptr(), plan.workspace_bytes,
+                                               torch.cuda.current_stream().cuda_stream)
+    assert st == bn.BITNET_OK
+    gy.check(f"persistent chain y ({junction})")
+    gw.check(f"persistent chain workspace ({junction})")
+    assert int(gw.t[:4].view(torch.int32).item()) == 0  # status: every wait succeeded
+    same(gy.t, chain.persistent(x), "persistent chain")
